@@ -1,0 +1,210 @@
+/*
+ * bi.h -- C ABI of libbi.so: batch-invariant RMSNorm, matmul and split-KV
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operations and the property they keep come from "Defeating
+ * Nondeterminism in LLM Inference" as summarised on mobiles-han.blogspot.com:
+ * the section defining batch invariance (one input always goes through the
+ * same computation strategy, whatever the batch size or concurrent work, and
+ * so gives the same bits) and the approach table, whose three rows are
+ * implemented here:
+ *   - RMSNorm: always data-parallel, one order for every batch size;
+ *   - MatMul: one kernel configuration, compiled ahead, for every shape;
+ *   - Attention: cache and current tokens in one layout before the cache is
+ *     read, and fixed-size splits independent of how the batch is made up.
+ *
+ * GUARANTEE.  For fixed logical inputs the output bits of every bi_* call do
+ * not depend on: the number of rows / M / sequences in the call, a row's or
+ * sequence's position in it, the other rows or sequences, how a prompt is
+ * chunked into prefill calls, prefill versus decode, which physical pages hold
+ * the keys, the stream, or how often the call is repeated.  Bits may differ
+ * between builds of this library.
+ *
+ * CONVENTIONS (all entry points).
+ *   - Every tensor argument is a DEVICE pointer to memory owned by the caller.
+ *     The library allocates nothing, frees nothing, never synchronises and
+ *     keeps no mutable global state; it is reentrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *     Inputs must stay alive and unmodified until that work completes.
+ *   - Host arguments are checked before anything is enqueued.  On any non-OK
+ *     status nothing has been enqueued.  Kernel faults surface, as usual in
+ *     HIP, at the caller's next synchronisation.
+ *   - bf16 tensors hold IEEE bfloat16 bit patterns; results are rounded to
+ *     nearest even.  Sizes of 0 are no-ops returning BI_OK; negative sizes are
+ *     BI_ERR_INVALID_SHAPE.
+ *   - Contents of device index arrays (kv_len, cu_q, block_table) are trusted:
+ *     entries outside the documented ranges are undefined behaviour.
+ *   - No C++ exception crosses this interface.
+ *   - Tensor pointers must be 16-byte aligned (BI_ERR_INVALID_SHAPE otherwise).
+ */
+#ifndef BI_H_
+#define BI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BI_ABI_VERSION 1
+
+typedef enum {
+  BI_OK = 0,
+  BI_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                   */
+  BI_ERR_INVALID_SHAPE = 2,       /* negative / inconsistent sizes, misalignment  */
+  BI_ERR_UNSUPPORTED = 3,         /* valid, but outside the one compiled config   */
+  BI_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the documented size    */
+  BI_ERR_HIP = 5,                 /* the HIP runtime refused a launch             */
+  BI_ERR_INTERNAL = 6
+} bi_status;
+
+typedef enum { BI_DTYPE_BF16 = 0, BI_DTYPE_F32 = 1 } bi_dtype;
+
+/* Version of this interface (BI_ABI_VERSION of the build). */
+int bi_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* bi_status_string(int status);
+
+/* ------------------------------------------------------------------------- */
+/* RMSNorm (approach table, RMSNorm row: data-parallel, one order per row).
+ *
+ *   rstd[r] = 1 / sqrt( (sum_c x[r,c]^2) / hidden + eps )
+ *   y[r,c]  = bf16( (x[r,c] * rstd[r]) * gamma[c] )
+ *
+ * x     bf16 [rows, hidden] row-major.
+ * gamma bf16 [hidden].
+ * y     bf16 [rows, hidden]; may equal x (in place); no other overlap.
+ * rstd  fp32 [rows], or NULL to skip.
+ * Each row is reduced by one workgroup in an order that depends on `hidden`
+ * only: per-lane sequential fp32 sums, a fixed wave64 butterfly, then the
+ * waves' partials added in wave order.
+ * Requires hidden % 8 == 0 and 8 <= hidden <= 16384 (else BI_ERR_UNSUPPORTED).
+ */
+int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+               int64_t hidden, float eps, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Matmul (approach table, MatMul row: one configuration for every shape).
+ *
+ *   c[i,j] = sum_k a[i,k] * w[k,j]     (fp32 accumulation; c bf16 or fp32)
+ *
+ * a  bf16 [m, k] row-major.
+ * w  bf16 [k, n] row-major (n contiguous).
+ * c  [m, n] row-major, bf16 (rounded from the fp32 sum) or fp32 per c_dtype.
+ * One compiled tile and one bf16 MFMA instruction for every m, n, k; each
+ * element's k-loop runs in one fixed order; no split-K.  The bf16 result is
+ * exactly the round-to-nearest-even of the fp32 result.
+ * Requires k % 64 == 0, n % 8 == 0 (else BI_ERR_UNSUPPORTED).
+ */
+int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
+              void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Paged attention (approach table, Attention row: one unified cache layout,
+ * fixed-size splits).
+ *
+ * Key/value pool: k_cache, v_cache bf16 [num_pages, num_kv_heads, page_size,
+ * head_dim].  Position p of sequence b lives in page block_table[b *
+ * max_pages_per_seq + p / page_size], slot p % page_size.
+ *
+ * Each call first appends the new tokens' keys and values to the pool, then
+ * computes attention reading keys and values from the pool only.  The query at
+ * absolute position p of a sequence attends to its positions 0..p.  Query
+ * head h reads kv head h / (num_q_heads / num_kv_heads).
+ *
+ * Keys are cut into fixed 256-position splits at absolute multiples of 256.
+ * For each split the partial (m_s, l_s, o_s) -- max logit, sum of exponentials,
+ * exponential-weighted sum of values -- is computed in one fixed order, and
+ * the partials are folded left in ascending split order:
+ *   m' = max(m, m_s);  l <- l e^(m-m') + l_s e^(m_s-m');  o <- o e^(m-m') + o_s e^(m_s-m')
+ *   out = bf16(o / l),  lse = m + ln(l)   (natural log, fp32)
+ * Prefill folds in registers; decode spreads splits over workgroups and folds
+ * them in a second kernel with the same function, so a token's row is bitwise
+ * the same through either entry point and any chunking.
+ */
+typedef struct {
+  int32_t num_seqs;          /* B >= 0                                         */
+  int32_t num_q_heads;       /* n_q, a multiple of num_kv_heads                */
+  int32_t num_kv_heads;      /* n_kv >= 1                                      */
+  int32_t head_dim;          /* d: 64 or 128                                   */
+  int32_t page_size;         /* must be 16                                     */
+  int32_t max_pages_per_seq; /* row stride of block_table                      */
+  int64_t num_pages;         /* pages in the pool                              */
+  float softmax_scale;       /* multiplies q.k, usually 1/sqrt(d)              */
+} bi_attn_shape;
+
+/* Split size in positions (fixed). */
+#define BI_ATTN_SPLIT 256
+
+/* Bytes of workspace bi_attn_decode needs for num_tokens (= num_seqs) queries
+ * whose sequences hold at most max_kv_len positions after the append.
+ * Returns 0 for invalid arguments. */
+size_t bi_attn_workspace_bytes(const bi_attn_shape* s, int64_t num_tokens, int32_t max_kv_len);
+
+/* Prefill (or any chunk): sequence b brings n_b = cu_q[b+1] - cu_q[b] new
+ * tokens, at positions kv_len[b] - n_b .. kv_len[b] - 1.
+ *   q      bf16 [total_q, n_q, d]     rows cu_q[b] .. cu_q[b+1]-1 are sequence b
+ *   k_new, v_new bf16 [total_q, n_kv, d]
+ *   cu_q   int32 [B + 1] device, cu_q[0] = 0, non-decreasing, cu_q[B] = total_q
+ *   kv_len int32 [B] device, length of each sequence AFTER this call's append
+ *   block_table int32 [B, max_pages_per_seq] device
+ *   out    bf16 [total_q, n_q, d];  lse fp32 [total_q, n_q] or NULL
+ *   max_q_per_seq (host) >= every n_b, used to size the grid.
+ * Requires n_b <= kv_len[b] <= max_pages_per_seq * page_size (trusted).
+ * No workspace. */
+int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+                    const int32_t* cu_q, const int32_t* kv_len, const int32_t* block_table,
+                    void* k_cache, void* v_cache, void* out, float* lse, int64_t total_q,
+                    int32_t max_q_per_seq, void* stream);
+
+/* Decode: one new token per sequence, at position kv_len[b] - 1.
+ *   q bf16 [B, n_q, d]; k_new, v_new bf16 [B, n_kv, d]; out bf16 [B, n_q, d];
+ *   lse fp32 [B, n_q] or NULL.
+ *   max_kv_len (host) >= every kv_len[b] (after the append), sizes the grid.
+ *   workspace: device, >= bi_attn_workspace_bytes(s, B, max_kv_len) bytes,
+ *   contents on entry ignored, scratch for the per-split partials. */
+int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+                   const int32_t* kv_len, const int32_t* block_table, void* k_cache,
+                   void* v_cache, void* out, float* lse, int32_t max_kv_len, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Non-invariant comparators (the strategies the approach table warns about).
+ * Same inputs and outputs as their bi_* counterparts; they exist to measure
+ * the cost of invariance and as negative controls: their results change with
+ * the batch.  Not for production use.
+ *
+ * bix_rmsnorm_splitrow: each row's sum of squares is split over `chunks`
+ * workgroups (chunks <= 0: chosen from `rows`, more chunks for fewer rows),
+ * partials added by a second kernel.  workspace >= rows * 64 * 4 bytes. */
+int bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+                         int64_t hidden, float eps, int32_t chunks, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* bix_matmul_splitk: the k range is split into `split_k` slices (split_k <= 0:
+ * chosen from m, n so that the grid fills the GPU), fp32 partials are summed
+ * in slice order by a second kernel.  workspace >= bix_matmul_workspace_bytes. */
+size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
+int bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
+                      int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* bix_attn_decode_splitkv: decode whose key range is cut into `num_splits`
+ * equal parts per sequence (num_splits <= 0: chosen from B and max_kv_len to
+ * fill the GPU), so split boundaries move with the batch.  workspace >=
+ * bix_attn_decode_workspace_bytes. */
+size_t bix_attn_decode_workspace_bytes(const bi_attn_shape* s, int32_t max_kv_len,
+                                       int32_t num_splits);
+int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k_new,
+                            const void* v_new, const int32_t* kv_len, const int32_t* block_table,
+                            void* k_cache, void* v_cache, void* out, float* lse,
+                            int32_t max_kv_len, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H_ */

@@ -1,0 +1,315 @@
+"""Batch-invariant RMSNorm, matmul and paged split-KV attention for MI355X.
+
+A thin ctypes binding over ``libbi.so`` (built from ``csrc/`` by ``_build.py``;
+the C interface and its contract are in ``include/bi.h``).  Every function
+here only checks and marshals arguments -- dtype, shape, contiguity, device --
+and hands raw device pointers plus torch's current HIP stream to the library.
+All arithmetic runs in the library's HIP kernels; torch is used only to hold
+device memory and streams.  If ``libbi.so`` is missing or cannot be loaded,
+every call raises: there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "BIError", "lib_path", "load", "abi_version", "rmsnorm", "matmul", "attn_workspace_bytes",
+    "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
+    "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
+]
+
+SPLIT = 256
+PAGE = 16
+DTYPE_BF16, DTYPE_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class BIError(RuntimeError):
+    """A libbi call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, text))
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    """Mirror of ``bi_attn_shape``."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+def lib_path() -> str:
+    return os.environ.get("BI_LIB", os.path.join(_HERE, "libbi.so"))
+
+
+def load():
+    """Load libbi.so (once).  Raises if it is absent: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError("libbi.so not found at %s; build it with "
+                           "`python -m invariant_bi_matmul_amd._build`" % path)
+    lib = ctypes.CDLL(path)
+    P, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                            ctypes.c_size_t)
+    SP = ctypes.POINTER(AttnShape)
+    sigs = {
+        "bi_abi_version": (ctypes.c_int, []),
+        "bi_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "bi_rmsnorm": (ctypes.c_int, [P, P, P, P, i64, i64, f32, P]),
+        "bi_matmul": (ctypes.c_int, [P, P, P, ctypes.c_int, i64, i64, i64, P]),
+        "bi_attn_workspace_bytes": (sz, [SP, i64, i32]),
+        "bi_attn_prefill": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
+        "bi_attn_decode": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, i32, P, sz, P]),
+        "bix_rmsnorm_splitrow": (ctypes.c_int, [P, P, P, P, i64, i64, f32, i32, P, sz, P]),
+        "bix_matmul_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "bix_matmul_splitk": (ctypes.c_int, [P, P, P, ctypes.c_int, i64, i64, i64, i32, P, sz, P]),
+        "bix_attn_decode_workspace_bytes": (sz, [SP, i32, i32]),
+        "bix_attn_decode_splitkv": (ctypes.c_int,
+                                    [SP, P, P, P, P, P, P, P, P, P, i32, i32, P, sz, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load().bi_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load().bi_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise BIError(fn, status, status_string(status))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+# --------------------------------------------------------------------------- RMSNorm
+
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6,
+            out: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None,
+            with_rstd: bool = False):
+    """y = bf16((x * rstd) * gamma), rstd = 1/sqrt(mean(x^2) + eps), per row.
+
+    x: bf16 [rows, hidden]; gamma: bf16 [hidden].  ``out`` may be ``x``.
+    Returns y, or (y, rstd) when ``with_rstd`` or ``rstd`` is given."""
+    _dev(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
+    rows, hidden = x.shape
+    _dev(gamma, "gamma", torch.bfloat16, (hidden,))
+    y = torch.empty_like(x) if out is None else _dev(out, "out", torch.bfloat16, x.shape)
+    if rstd is None and with_rstd:
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device)
+    if rstd is not None:
+        _dev(rstd, "rstd", torch.float32, (rows,))
+    _check("bi_rmsnorm", load().bi_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), rows, hidden,
+                                           float(eps), _stream()))
+    return (y, rstd) if rstd is not None else y
+
+
+def bix_rmsnorm_splitrow(x, gamma, eps=1e-6, chunks: int = 0, out=None, rstd=None,
+                         workspace=None):
+    """Non-invariant comparator: each row's reduction split over ``chunks``
+    workgroups (0 = chosen from the row count)."""
+    _dev(x, "x", torch.bfloat16)
+    rows, hidden = x.shape
+    _dev(gamma, "gamma", torch.bfloat16, (hidden,))
+    y = torch.empty_like(x) if out is None else _dev(out, "out", torch.bfloat16, x.shape)
+    if rstd is not None:
+        _dev(rstd, "rstd", torch.float32, (rows,))
+    if workspace is None:
+        workspace = torch.empty(max(rows, 1) * 64, dtype=torch.float32, device=x.device)
+    _check("bix_rmsnorm_splitrow", load().bix_rmsnorm_splitrow(
+        _ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), rows, hidden, float(eps), int(chunks),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return (y, rstd) if rstd is not None else y
+
+
+# --------------------------------------------------------------------------- matmul
+
+def matmul(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
+           out_dtype: torch.dtype = torch.bfloat16):
+    """C = A @ W; a bf16 [m, k], w bf16 [k, n] (n contiguous); C bf16 or fp32."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[0]:
+        raise ValueError("need a [m, k] and w [k, n]")
+    m, k = a.shape
+    n = w.shape[1]
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    c = torch.empty(m, n, dtype=out_dtype, device=a.device) if out is None else \
+        _dev(out, "out", out_dtype, (m, n))
+    code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
+    _check("bi_matmul", load().bi_matmul(_ptr(a), _ptr(w), _ptr(c), code, m, n, k, _stream()))
+    return c
+
+
+def bix_matmul_splitk(a, w, split_k: int = 0, out=None, out_dtype=torch.bfloat16,
+                      workspace=None):
+    """Non-invariant comparator: split-K with ``split_k`` slices (0 = chosen
+    from the grid size)."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    m, k = a.shape
+    n = w.shape[1]
+    c = torch.empty(m, n, dtype=out_dtype, device=a.device) if out is None else \
+        _dev(out, "out", out_dtype, (m, n))
+    lib = load()
+    need = lib.bix_matmul_workspace_bytes(m, n, k, int(split_k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=a.device)
+    code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
+    _check("bix_matmul_splitk", lib.bix_matmul_splitk(
+        _ptr(a), _ptr(w), _ptr(c), code, m, n, k, int(split_k), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return c
+
+
+# --------------------------------------------------------------------------- attention
+
+def make_shape(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+               max_pages_per_seq: int, num_pages: int, softmax_scale: float) -> AttnShape:
+    return AttnShape(num_seqs, num_q_heads, num_kv_heads, head_dim, PAGE, max_pages_per_seq,
+                     num_pages, softmax_scale)
+
+
+def _cache_shape(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    _dev(k_cache, "k_cache", torch.bfloat16)
+    _dev(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    if k_cache.dim() != 4 or k_cache.shape[2] != PAGE:
+        raise ValueError("caches must be [num_pages, n_kv, 16, d]")
+    return k_cache.shape
+
+
+def attn_workspace_bytes(shape: AttnShape, num_tokens: int, max_kv_len: int) -> int:
+    return int(load().bi_attn_workspace_bytes(ctypes.byref(shape), num_tokens, max_kv_len))
+
+
+def attn_prefill(q, k_new, v_new, cu_q, kv_len, block_table, k_cache, v_cache, softmax_scale,
+                 max_q_per_seq: int, out=None, lse=None, with_lse: bool = False):
+    """Append k_new/v_new to the paged caches, then causal attention for q.
+
+    q bf16 [T, n_q, d]; k_new/v_new bf16 [T, n_kv, d]; cu_q int32 [B+1];
+    kv_len int32 [B] (after the append); block_table int32 [B, max_pages];
+    caches bf16 [P, n_kv, 16, d].  Returns out (and lse)."""
+    P, nkv, _, d = _cache_shape(k_cache, v_cache)
+    _dev(q, "q", torch.bfloat16)
+    T, nq, dq = q.shape
+    if dq != d:
+        raise ValueError("head_dim mismatch")
+    _dev(k_new, "k_new", torch.bfloat16, (T, nkv, d))
+    _dev(v_new, "v_new", torch.bfloat16, (T, nkv, d))
+    _dev(block_table, "block_table", torch.int32)
+    B, maxp = block_table.shape
+    _dev(cu_q, "cu_q", torch.int32, (B + 1,))
+    _dev(kv_len, "kv_len", torch.int32, (B,))
+    o = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16, q.shape)
+    if lse is None and with_lse:
+        lse = torch.empty(T, nq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (T, nq))
+    shape = make_shape(B, nq, nkv, d, maxp, P, softmax_scale)
+    _check("bi_attn_prefill", load().bi_attn_prefill(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_q), _ptr(kv_len),
+        _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), T,
+        int(max_q_per_seq), _stream()))
+    return (o, lse) if lse is not None else o
+
+
+def _decode_args(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse, with_lse):
+    P, nkv, _, d = _cache_shape(k_cache, v_cache)
+    _dev(q, "q", torch.bfloat16)
+    B, nq, dq = q.shape
+    if dq != d:
+        raise ValueError("head_dim mismatch")
+    _dev(k_new, "k_new", torch.bfloat16, (B, nkv, d))
+    _dev(v_new, "v_new", torch.bfloat16, (B, nkv, d))
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table needs one row per sequence")
+    _dev(kv_len, "kv_len", torch.int32, (B,))
+    o = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16, q.shape)
+    if lse is None and with_lse:
+        lse = torch.empty(B, nq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, nq))
+    return B, nq, nkv, d, P, block_table.shape[1], o, lse
+
+
+def attn_decode(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, softmax_scale,
+                max_kv_len: int, workspace=None, out=None, lse=None, with_lse: bool = False):
+    """One new token per sequence: append, then split-parallel attention with a
+    fixed-order combine.  q bf16 [B, n_q, d]; k_new/v_new bf16 [B, n_kv, d]."""
+    B, nq, nkv, d, P, maxp, o, lse = _decode_args(q, k_new, v_new, kv_len, block_table, k_cache,
+                                                  v_cache, out, lse, with_lse)
+    shape = make_shape(B, nq, nkv, d, maxp, P, softmax_scale)
+    lib = load()
+    need = lib.bi_attn_workspace_bytes(ctypes.byref(shape), B, int(max_kv_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    _check("bi_attn_decode", lib.bi_attn_decode(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_len), _ptr(block_table),
+        _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(max_kv_len), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return (o, lse) if lse is not None else o
+
+
+def bix_attn_decode_splitkv(q, k_new, v_new, kv_len, block_table, k_cache, v_cache,
+                            softmax_scale, max_kv_len: int, num_splits: int = 0, workspace=None,
+                            out=None, lse=None, with_lse: bool = False):
+    """Non-invariant comparator: decode with a split count chosen from the
+    batch (0 = the library's heuristic)."""
+    B, nq, nkv, d, P, maxp, o, lse = _decode_args(q, k_new, v_new, kv_len, block_table, k_cache,
+                                                  v_cache, out, lse, with_lse)
+    shape = make_shape(B, nq, nkv, d, maxp, P, softmax_scale)
+    lib = load()
+    need = lib.bix_attn_decode_workspace_bytes(ctypes.byref(shape), int(max_kv_len),
+                                               int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    _check("bix_attn_decode_splitkv", lib.bix_attn_decode_splitkv(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_len), _ptr(block_table),
+        _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(max_kv_len), int(num_splits),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return (o, lse) if lse is not None else o

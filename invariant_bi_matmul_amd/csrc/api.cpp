@@ -1,0 +1,290 @@
+// extern "C" entry points of libbi.so (declared and documented in bi.h).
+//
+// Every entry point checks its host arguments completely before it enqueues
+// anything, then launches on the caller's stream.  Nothing here allocates,
+// synchronises or keeps state.
+#include "bi.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
+
+constexpr int64_t kMaxGridX = 0x7fffffff;
+constexpr int64_t kMaxGridYZ = 65535;
+
+// Checks shared by the attention entry points.
+int check_attn_shape(const bi_attn_shape* s) {
+  if (s == nullptr) return BI_ERR_NULL_POINTER;
+  if (s->num_seqs < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0 || s->head_dim <= 0 ||
+      s->max_pages_per_seq <= 0 || s->num_pages <= 0)
+    return BI_ERR_INVALID_SHAPE;
+  if (s->num_q_heads % s->num_kv_heads != 0) return BI_ERR_INVALID_SHAPE;
+  const int group = s->num_q_heads / s->num_kv_heads;
+  if (group > 16 || (16 % group) != 0) return BI_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return BI_ERR_UNSUPPORTED;
+  if (s->page_size != bi::kPage) return BI_ERR_UNSUPPORTED;
+  if (!(s->softmax_scale > 0.0f) || !isfinite(s->softmax_scale)) return BI_ERR_INVALID_SHAPE;
+  if (s->num_seqs > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
+  return BI_OK;
+}
+
+bi::AttnDims dims_of(const bi_attn_shape* s) {
+  return bi::AttnDims{s->num_seqs, s->num_q_heads, s->num_kv_heads, s->head_dim,
+                      s->max_pages_per_seq, s->softmax_scale};
+}
+
+size_t decode_ws_bytes(const bi_attn_shape* s, int64_t tokens, int64_t nsplit) {
+  return (size_t)tokens * (size_t)s->num_q_heads * (size_t)nsplit * (size_t)(s->head_dim + 2) *
+         sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bi_abi_version(void) { return BI_ABI_VERSION; }
+
+const char* bi_status_string(int status) {
+  switch (status) {
+    case BI_OK: return "ok";
+    case BI_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case BI_ERR_INVALID_SHAPE: return "invalid or inconsistent sizes, or a misaligned pointer";
+    case BI_ERR_UNSUPPORTED: return "outside the one compiled configuration";
+    case BI_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than required";
+    case BI_ERR_HIP: return "the HIP runtime refused a launch";
+    case BI_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+// ---------------------------------------------------------------------------
+static int check_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+                         int64_t hidden) {
+  if (rows < 0 || hidden < 0) return BI_ERR_INVALID_SHAPE;
+  if (hidden % 8 != 0 || hidden < 8 || hidden > 16384) return BI_ERR_UNSUPPORTED;
+  if (rows > kMaxGridX) return BI_ERR_UNSUPPORTED;
+  if (rows == 0) return -1;  // no-op
+  if (x == nullptr || gamma == nullptr || y == nullptr) return BI_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(y) || !aligned4(rstd))
+    return BI_ERR_INVALID_SHAPE;
+  return BI_OK;
+}
+
+int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+               int64_t hidden, float eps, void* stream) {
+  try {
+    const int c = check_rmsnorm(x, gamma, y, rstd, rows, hidden);
+    if (c < 0) return BI_OK;
+    if (c != BI_OK) return c;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(
+        bi::launch_rmsnorm(x, gamma, y, rstd, rows, (int)hidden, eps, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+                         int64_t hidden, float eps, int32_t chunks, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  try {
+    const int c = check_rmsnorm(x, gamma, y, rstd, rows, hidden);
+    if (c < 0) return BI_OK;
+    if (c != BI_OK) return c;
+    if (!(eps >= 0.0f) || !isfinite(eps)) return BI_ERR_INVALID_SHAPE;
+    if (chunks <= 0) chunks = bi::rmsnorm_splitrow_auto_chunks(rows);
+    if (chunks > 64 || chunks > hidden / 8) return BI_ERR_UNSUPPORTED;
+    if (workspace == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned4(workspace)) return BI_ERR_INVALID_SHAPE;
+    if (workspace_bytes < (size_t)rows * 64 * sizeof(float)) return BI_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(bi::launch_rmsnorm_splitrow(x, gamma, y, rstd, rows, (int)hidden, eps,
+                                                  chunks, (float*)workspace,
+                                                  (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+// ---------------------------------------------------------------------------
+static int check_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
+                        int64_t k) {
+  if (m < 0 || n < 0 || k < 0) return BI_ERR_INVALID_SHAPE;
+  if (c_dtype != BI_DTYPE_BF16 && c_dtype != BI_DTYPE_F32) return BI_ERR_INVALID_SHAPE;
+  if (k % bi::kMatmulBK != 0 || n % 8 != 0) return BI_ERR_UNSUPPORTED;
+  if (m > 0x7fffffff || n > 0x7fffffff || k > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return -1;
+  if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGridX) return BI_ERR_UNSUPPORTED;
+  if (c == nullptr || (k > 0 && (a == nullptr || w == nullptr))) return BI_ERR_NULL_POINTER;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return BI_ERR_INVALID_SHAPE;
+  return BI_OK;
+}
+
+int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
+              void* stream) {
+  try {
+    const int s = check_matmul(a, w, c, c_dtype, m, n, k);
+    if (s < 0) return BI_OK;
+    if (s != BI_OK) return s;
+    return hip_status(
+        bi::launch_matmul(a, w, c, c_dtype == BI_DTYPE_F32, m, n, k, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
+  if (m < 0 || n < 0 || k < 0 || k % bi::kMatmulBK != 0) return 0;
+  if (split_k <= 0) split_k = bi::matmul_splitk_auto(m, n, k);
+  if (split_k < 1) split_k = 1;
+  return (size_t)split_k * (size_t)m * (size_t)n * sizeof(float);
+}
+
+int bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
+                      int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  try {
+    const int s = check_matmul(a, w, c, c_dtype, m, n, k);
+    if (s < 0) return BI_OK;
+    if (s != BI_OK) return s;
+    if (k == 0) return BI_ERR_UNSUPPORTED;
+    if (split_k <= 0) split_k = bi::matmul_splitk_auto(m, n, k);
+    if (split_k > k / bi::kMatmulBK || split_k > 65535) return BI_ERR_UNSUPPORTED;
+    if (workspace == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(workspace)) return BI_ERR_INVALID_SHAPE;
+    if (workspace_bytes < (size_t)split_k * (size_t)m * (size_t)n * sizeof(float))
+      return BI_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(bi::launch_matmul_splitk(a, w, c, c_dtype == BI_DTYPE_F32, m, n, k, split_k,
+                                               (float*)workspace, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+// ---------------------------------------------------------------------------
+size_t bi_attn_workspace_bytes(const bi_attn_shape* s, int64_t num_tokens, int32_t max_kv_len) {
+  if (check_attn_shape(s) != BI_OK || num_tokens < 0 || max_kv_len < 0) return 0;
+  const int64_t ns = ((int64_t)max_kv_len + bi::kSplit - 1) / bi::kSplit;
+  return decode_ws_bytes(s, num_tokens, ns > 0 ? ns : 1);
+}
+
+int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+                    const int32_t* cu_q, const int32_t* kv_len, const int32_t* block_table,
+                    void* k_cache, void* v_cache, void* out, float* lse, int64_t total_q,
+                    int32_t max_q_per_seq, void* stream) {
+  try {
+    const int c = check_attn_shape(s);
+    if (c != BI_OK) return c;
+    if (total_q < 0 || max_q_per_seq < 0) return BI_ERR_INVALID_SHAPE;
+    if (s->num_seqs == 0 || total_q == 0 || max_q_per_seq == 0) return BI_OK;
+    if (max_q_per_seq > total_q) return BI_ERR_INVALID_SHAPE;
+    if (max_q_per_seq > (int64_t)s->max_pages_per_seq * s->page_size) return BI_ERR_INVALID_SHAPE;
+    if (total_q > kMaxGridX) return BI_ERR_UNSUPPORTED;
+    if (!q || !k_new || !v_new || !cu_q || !kv_len || !block_table || !k_cache || !v_cache || !out)
+      return BI_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out) || !aligned4(lse) || !aligned4(cu_q) ||
+        !aligned4(kv_len) || !aligned4(block_table))
+      return BI_ERR_INVALID_SHAPE;
+    const bi::AttnDims d = dims_of(s);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bi::launch_kv_append(d, k_new, v_new, cu_q, kv_len, block_table, k_cache,
+                                        v_cache, max_q_per_seq, st);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    return hip_status(bi::launch_attn_prefill(d, q, cu_q, kv_len, block_table, k_cache, v_cache,
+                                              out, lse, max_q_per_seq, st));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+static int check_decode(const bi_attn_shape* s, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* kv_len, const int32_t* block_table,
+                        void* k_cache, void* v_cache, void* out, float* lse, int32_t max_kv_len,
+                        void* workspace) {
+  const int c = check_attn_shape(s);
+  if (c != BI_OK) return c;
+  if (max_kv_len < 0) return BI_ERR_INVALID_SHAPE;
+  if (s->num_seqs == 0) return -1;
+  if (max_kv_len < 1 || max_kv_len > (int64_t)s->max_pages_per_seq * s->page_size)
+    return BI_ERR_INVALID_SHAPE;
+  if (!q || !k_new || !v_new || !kv_len || !block_table || !k_cache || !v_cache || !out ||
+      !workspace)
+    return BI_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || !aligned4(lse) || !aligned4(kv_len) ||
+      !aligned4(block_table) || !aligned16(workspace))
+    return BI_ERR_INVALID_SHAPE;
+  return BI_OK;
+}
+
+int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+                   const int32_t* kv_len, const int32_t* block_table, void* k_cache,
+                   void* v_cache, void* out, float* lse, int32_t max_kv_len, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  try {
+    const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
+                               max_kv_len, workspace);
+    if (c < 0) return BI_OK;
+    if (c != BI_OK) return c;
+    const int ns = (max_kv_len + bi::kSplit - 1) / bi::kSplit;
+    if (workspace_bytes < decode_ws_bytes(s, s->num_seqs, ns)) return BI_ERR_WORKSPACE_TOO_SMALL;
+    if ((int64_t)s->num_seqs * s->num_kv_heads * ns / 4 + 1 > kMaxGridX) return BI_ERR_UNSUPPORTED;
+    const bi::AttnDims d = dims_of(s);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
+                                        v_cache, 1, st);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
+                                             ns, (float*)workspace, st));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+size_t bix_attn_decode_workspace_bytes(const bi_attn_shape* s, int32_t max_kv_len,
+                                       int32_t num_splits) {
+  if (check_attn_shape(s) != BI_OK || max_kv_len < 1) return 0;
+  if (num_splits <= 0) num_splits = bi::attn_splitkv_auto(s->num_seqs, s->num_kv_heads, max_kv_len);
+  int64_t len = ((int64_t)max_kv_len + num_splits - 1) / num_splits;
+  len = (len + 31) / 32 * 32;
+  const int64_t ns = ((int64_t)max_kv_len + len - 1) / len;
+  return decode_ws_bytes(s, s->num_seqs, ns);
+}
+
+int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k_new,
+                            const void* v_new, const int32_t* kv_len, const int32_t* block_table,
+                            void* k_cache, void* v_cache, void* out, float* lse,
+                            int32_t max_kv_len, int32_t num_splits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  try {
+    const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
+                               max_kv_len, workspace);
+    if (c < 0) return BI_OK;
+    if (c != BI_OK) return c;
+    if (num_splits <= 0)
+      num_splits = bi::attn_splitkv_auto(s->num_seqs, s->num_kv_heads, max_kv_len);
+    if (num_splits > max_kv_len) return BI_ERR_UNSUPPORTED;
+    if (workspace_bytes < bix_attn_decode_workspace_bytes(s, max_kv_len, num_splits))
+      return BI_ERR_WORKSPACE_TOO_SMALL;
+    const bi::AttnDims d = dims_of(s);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
+                                        v_cache, 1, st);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    return hip_status(bi::launch_attn_decode_splitkv(d, q, kv_len, block_table, k_cache, v_cache,
+                                                     out, lse, max_kv_len, num_splits,
+                                                     (float*)workspace, st));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Device helpers shared by the libbi kernels (gfx950, wave64).
+//
+// Numerics policy for every kernel of the library: built with
+// -ffp-contract=off and without fast-math, so a*b+c is always a rounded
+// multiply followed by a rounded add unless a kernel asks for fmaf.  bf16
+// results are rounded to nearest even by f32_to_bf16 below, the one
+// conversion used everywhere.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Low halves / high halves of two packed bf16 pairs: (lo16(a), lo16(b)) etc.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+// Lane l: A row l%32, k = 8*(l/32)+0..7; B col l%32, same k;
+// D col l%32, rows 8*(r/4) + 4*(l/32) + r%4 for register r.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16), bf16 in, fp32 accumulate.
+// Lane l: A row l%16, k = 8*(l/16)+0..7; B col l%16, same k;
+// D col l%16, rows 4*(l/16) + r for register r.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (XCD = id % 8).
+// Renumber so that each XCD receives one contiguous range of logical ids,
+// which keeps neighbouring tiles in one XCD's L2.  A bijection for any count.
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t bid, uint32_t nwg) {
+  const uint32_t q = nwg / 8u, r = nwg % 8u;
+  const uint32_t xcd = bid % 8u, local = bid / 8u;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+}  // namespace bi

@@ -1,0 +1,52 @@
+// Internal launchers behind the C ABI.  Each returns hipGetLastError() of its
+// launches; argument checking happens in api.cpp before any of these runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bi {
+
+// ---- RMSNorm -------------------------------------------------------------
+hipError_t launch_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+                          int hidden, float eps, hipStream_t st);
+hipError_t launch_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd,
+                                   int64_t rows, int hidden, float eps, int chunks, float* ws,
+                                   hipStream_t st);
+int rmsnorm_splitrow_auto_chunks(int64_t rows);
+
+// ---- matmul ----------------------------------------------------------------
+constexpr int kMatmulBK = 64;
+hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
+                         int64_t k, hipStream_t st);
+int matmul_splitk_auto(int64_t m, int64_t n, int64_t k);
+hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,
+                                int64_t n, int64_t k, int split_k, float* ws, hipStream_t st);
+
+// ---- attention -------------------------------------------------------------
+constexpr int kSplit = 256;   // fixed key split
+constexpr int kPage = 16;     // tokens per page
+
+struct AttnDims {
+  int B, nq, nkv, d, max_pages;
+  float scale;
+};
+
+hipError_t launch_kv_append(const AttnDims& s, const void* k_new, const void* v_new,
+                            const int32_t* cu_q, const int32_t* kv_len, const int32_t* bt,
+                            void* kc, void* vc, int max_q_per_seq, hipStream_t st);
+hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* cu_q,
+                               const int32_t* kv_len, const int32_t* bt, const void* kc,
+                               const void* vc, void* out, float* lse, int max_q_per_seq,
+                               hipStream_t st);
+hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
+                              const int32_t* bt, const void* kc, const void* vc, void* out,
+                              float* lse, int max_splits, float* ws, hipStream_t st);
+hipError_t launch_attn_decode_splitkv(const AttnDims& s, const void* q, const int32_t* kv_len,
+                                      const int32_t* bt, const void* kc, const void* vc, void* out,
+                                      float* lse, int max_kv_len, int num_splits, float* ws,
+                                      hipStream_t st);
+int attn_splitkv_auto(int B, int nkv, int max_kv_len);
+
+}  // namespace bi

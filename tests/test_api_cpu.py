@@ -1,0 +1,103 @@
+"""The C-ABI library without a GPU: it loads, exports every function bi.h
+declares, and rejects bad arguments with the documented status before any
+HIP call (so these run on a host with no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi.h")
+
+OK, NULLP, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:bi|bix)_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import invariant_bi_matmul_amd as bi
+    if not os.path.exists(bi.lib_path()):
+        pytest.fail("libbi.so is not built (python -m invariant_bi_matmul_amd._build)")
+    return bi.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert "bi_matmul" in names and "bi_attn_decode" in names and len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.bi_abi_version() == 1
+    for s in range(7):
+        assert lib.bi_status_string(s)
+    assert lib.bi_status_string(99) == b"unknown status"
+
+
+def _p(v=0x1000):
+    return ctypes.c_void_p(v)
+
+
+def test_rmsnorm_validation(lib):
+    f = lib.bi_rmsnorm
+    assert f(_p(), _p(), _p(), None, -1, 4096, 1e-6, None) == SHAPE
+    assert f(_p(), _p(), _p(), None, 4, 4100, 1e-6, None) == UNSUP
+    assert f(_p(), _p(), _p(), None, 4, 32768, 1e-6, None) == UNSUP
+    assert f(None, _p(), _p(), None, 4, 4096, 1e-6, None) == NULLP
+    assert f(_p(0x1008), _p(), _p(), None, 4, 4096, 1e-6, None) == SHAPE
+    assert f(_p(), _p(), _p(), None, 4, 4096, -1.0, None) == SHAPE
+    assert f(None, None, None, None, 0, 4096, 1e-6, None) == OK  # empty: no-op
+    assert lib.bix_rmsnorm_splitrow(_p(), _p(), _p(), None, 4, 4096, 1e-6, 2, _p(), 16,
+                                    None) == WS
+
+
+def test_matmul_validation(lib):
+    f = lib.bi_matmul
+    assert f(_p(), _p(), _p(), 0, 4, 4096, 100, None) == UNSUP      # k % 64
+    assert f(_p(), _p(), _p(), 0, 4, 4100, 4096, None) == UNSUP     # n % 8
+    assert f(_p(), _p(), _p(), 7, 4, 4096, 4096, None) == SHAPE     # dtype
+    assert f(_p(), _p(), _p(), 0, -4, 4096, 4096, None) == SHAPE
+    assert f(_p(), None, _p(), 0, 4, 4096, 4096, None) == NULLP
+    assert f(None, None, None, 0, 0, 4096, 4096, None) == OK
+    assert lib.bix_matmul_workspace_bytes(8, 4096, 4096, 4) == 4 * 8 * 4096 * 4
+    assert lib.bix_matmul_splitk(_p(), _p(), _p(), 0, 8, 4096, 4096, 4, _p(), 1024, None) == WS
+
+
+def _shape(**kw):
+    import invariant_bi_matmul_amd as bi
+    base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
+                num_pages=8, softmax_scale=0.088388346)
+    base.update(kw)
+    s = bi.make_shape(**base)
+    return s
+
+
+def test_attention_validation(lib):
+    import invariant_bi_matmul_amd as bi
+    s = _shape()
+    by = ctypes.byref
+    assert lib.bi_attn_workspace_bytes(by(s), 2, 300) == 2 * 32 * 2 * 130 * 4
+    assert lib.bi_attn_workspace_bytes(by(_shape(head_dim=96)), 2, 300) == 0
+    args = [_p()] * 9 + [None]
+    assert lib.bi_attn_prefill(by(_shape(head_dim=96)), *args, 10, 5, None) == UNSUP
+    assert lib.bi_attn_prefill(by(_shape(num_kv_heads=5)), *args, 10, 5, None) == SHAPE
+    assert lib.bi_attn_prefill(by(_shape(num_q_heads=64, num_kv_heads=2)), *args, 10, 5,
+                               None) == UNSUP  # group 32 > 16
+    bad_page = _shape()
+    bad_page.page_size = 32
+    assert lib.bi_attn_prefill(by(bad_page), *args, 10, 5, None) == UNSUP
+    assert lib.bi_attn_prefill(by(s), *args, 10, 65, None) == SHAPE  # > 4 pages * 16
+    assert lib.bi_attn_prefill(by(s), *([None] + [_p()] * 8 + [None]), 10, 5, None) == NULLP
+    assert lib.bi_attn_prefill(by(s), *args, 0, 0, None) == OK
+    dec = [_p()] * 8 + [None]
+    assert lib.bi_attn_decode(by(s), *dec, 60, _p(), 16, None) == WS
+    assert lib.bi_attn_decode(by(s), *dec, 65, _p(), 1 << 30, None) == SHAPE
+    assert lib.bi_attn_decode(by(_shape(num_seqs=0)), *dec, 0, None, 0, None) == OK
+    assert bi.SPLIT == 256 and bi.PAGE == 16

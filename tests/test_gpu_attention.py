@@ -1,0 +1,177 @@
+"""Paged attention on the GPU: parity with the fp64 oracle and bitwise
+invariance across chunkings, prefill vs decode, batch companions, batch
+position and physical page placement."""
+import numpy as np
+import pytest
+
+import synth
+from helpers import (TOL_BF16, TOL_F32, PagedRun, f64, lse_err, oracle_attention, rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(orc, prob, run, picks):
+    out, lse = oracle_attention(orc, prob, picks)
+    got = np.stack([run.out[b][p] for b, p in picks])
+    glse = np.stack([run.lse[b][p] for b, p in picks])
+    assert rel_err(f64(got), out) < TOL_BF16
+    assert lse_err(glse, lse) < TOL_F32
+
+
+# ---- toy decoder block: 4 heads, d=64, causal, seq 128 ------------------------
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_toy_whole_vs_chunks_of_32(orc, B):
+    prob = synth.attn_problem([128] * B, n_q=4, n_kv=4, d=64, seed=0)
+    whole = PagedRun(prob, page_seed=1)
+    whole.prefill([(b, 128) for b in range(B)])
+    chunked = PagedRun(prob, page_seed=2)
+    chunked.run_chunked(32)
+    for b in range(B):
+        assert np.array_equal(whole.out[b], chunked.out[b])
+        assert np.array_equal(whole.lse[b].view(np.uint32), chunked.lse[b].view(np.uint32))
+    _parity(orc, prob, whole, [(b, p) for b in range(B) for p in range(128)])
+
+
+def test_toy_row0_across_batch_sizes():
+    ref = None
+    for B in (1, 3, 8):
+        prob = synth.attn_problem([128] * B, n_q=4, n_kv=4, d=64, seed=0)
+        run = PagedRun(prob, page_seed=B)
+        run.run_chunked(32 if B == 3 else 128)
+        if ref is None:
+            ref = run.out[0].copy()
+        assert np.array_equal(run.out[0], ref)
+
+
+# ---- GQA 32/8, d=128 ------------------------------------------------------------
+
+def _gqa(lens, seed=0, tags=None):
+    return synth.attn_problem(lens, n_q=32, n_kv=8, d=128, seed=seed, tags=tags)
+
+
+BOUNDARY = (0, 1, 255, 256, 257, 511)
+
+
+def test_gqa_512_chunkings_and_decode_equal_one_shot(orc):
+    lens, _ = synth.ragged_lengths(4, 512, seed=0)
+    prob = _gqa(lens)
+    one = PagedRun(prob, page_seed=10)
+    one.prefill([(b, L) for b, L in enumerate(lens)])
+    picks = [(b, p) for b, L in enumerate(lens) for p in BOUNDARY + (L - 1,) if p < L]
+    _parity(orc, prob, one, picks)
+    for chunk in (512, 128, 100, 33, 1):
+        run = PagedRun(prob, page_seed=11 + chunk)
+        run.run_chunked(chunk)
+        for b in range(len(lens)):
+            assert np.array_equal(run.out[b], one.out[b]), (chunk, b)
+            assert np.array_equal(run.lse[b].view(np.uint32), one.lse[b].view(np.uint32))
+    # prefill most of each sequence, then decode the rest one token per call
+    dec = PagedRun(prob, page_seed=99)
+    dec.prefill([(b, L - 40) for b, L in enumerate(lens)])
+    for _ in range(40):
+        dec.decode(list(range(len(lens))))
+    for b in range(len(lens)):
+        assert np.array_equal(dec.out[b], one.out[b]), b
+        assert np.array_equal(dec.lse[b].view(np.uint32), one.lse[b].view(np.uint32))
+
+
+def test_gqa_4096_chunked_prefill_then_decode(orc):
+    lens = [4096, 3001]
+    prob = _gqa(lens, seed=1)
+    one = PagedRun(prob, page_seed=3)
+    one.prefill([(b, L) for b, L in enumerate(lens)])
+    picks = [(0, p) for p in (0, 255, 256, 1023, 2048, 4095)] + [(1, 3000), (1, 2999)]
+    _parity(orc, prob, one, picks)
+    run = PagedRun(prob, page_seed=4)
+    # 512-token chunks for all but the last 16 tokens, which are decoded
+    while True:
+        items = [(b, min(512, L - 16 - run.cur[b])) for b, L in enumerate(lens)
+                 if run.cur[b] < L - 16]
+        if not items:
+            break
+        run.prefill(items)
+    for _ in range(16):
+        run.decode([0, 1])
+    for b in range(2):
+        assert np.array_equal(run.out[b], one.out[b])
+
+
+def test_decode_batch_companions_and_position():
+    """A probe sequence's decode rows are the same alone and among 15
+    companions at any batch index, with different page placements."""
+    L = 1000
+    comp_lens, _ = synth.ragged_lengths(15, 1024, seed=5)
+    results = []
+    for idx, page_seed in ((None, 0), (0, 1), (7, 2), (15, 3)):
+        if idx is None:
+            lens, tags = [L], ["probe"]
+        else:
+            lens = comp_lens[:idx] + [L] + comp_lens[idx:]
+            tags = ["c%d" % i for i in range(idx)] + ["probe"] + ["c%d" % i for i in range(idx, 15)]
+        prob = _gqa(lens, seed=7, tags=tags)
+        run = PagedRun(prob, page_seed=page_seed)
+        run.prefill([(b, n - 3) for b, n in enumerate(lens)])
+        for _ in range(3):
+            run.decode(list(range(len(lens))))
+        pb = 0 if idx is None else idx
+        results.append(run.out[pb][L - 3:].copy())
+    for r in results[1:]:
+        assert np.array_equal(r, results[0])
+
+
+def test_long_context_32768(orc):
+    L = 32768
+    prob = _gqa([L], seed=9)
+    one = PagedRun(prob, page_seed=5)
+    one.prefill([(0, L)])
+    picks = [(0, p) for p in (0, 256, 4096, 20000, 32767)]
+    _parity(orc, prob, one, picks)
+    dec = PagedRun(prob, page_seed=6)
+    dec.run_chunked(8192)
+    assert np.array_equal(dec.out[0], one.out[0])
+    tail = PagedRun(prob, page_seed=7)
+    tail.prefill([(0, L - 2)])
+    tail.decode([0])
+    tail.decode([0])
+    assert np.array_equal(tail.out[0][L - 2:], one.out[0][L - 2:])
+
+
+def test_pins_position0_and_uniform(orc):
+    d, nq, nkv = 128, 32, 8
+    L = 300
+    q, k, v = synth.attn_seq(L, nq, nkv, d, seed=3, tag="pin")
+    prob = synth.AttnProblem([L], nq, nkv, d, [np.zeros_like(q)], [k], [v])
+    run = PagedRun(prob, page_seed=8)
+    run.prefill([(0, L)])
+    grp = nq // nkv
+    # position 0: weight exactly 1 on key 0 -> out == V[0] bitwise
+    for h in range(nq):
+        assert np.array_equal(run.out[0][0, h], v[0, h // grp])
+    # Q = 0: uniform weights, lse = ln(p + 1)
+    for p in (1, 255, 256, 299):
+        mean = f64(v[:p + 1]).mean(axis=0)  # [nkv, d]
+        expect = np.repeat(mean, grp, axis=0)
+        assert rel_err(f64(run.out[0][p]), expect) < TOL_BF16
+        np.testing.assert_allclose(run.lse[0][p], np.log(p + 1), rtol=TOL_F32)
+    # real queries at position 0 too
+    prob2 = synth.AttnProblem([L], nq, nkv, d, [q], [k], [v])
+    run2 = PagedRun(prob2, page_seed=9)
+    run2.prefill([(0, 64)])
+    for h in range(nq):
+        assert np.array_equal(run2.out[0][0, h], v[0, h // grp])
+
+
+def test_repeat_bitwise():
+    lens, _ = synth.ragged_lengths(8, 2048, seed=11)
+    prob = _gqa(lens, seed=11)
+    base = None
+    for rep in range(5):
+        run = PagedRun(prob, page_seed=rep)
+        run.prefill([(b, L - 1) for b, L in enumerate(lens)])
+        run.decode(list(range(8)))
+        cur = [o.copy() for o in run.out]
+        if base is None:
+            base = cur
+        for a, b in zip(base, cur):
+            assert np.array_equal(a, b)
