@@ -1,0 +1,383 @@
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of Llama-8B-shaped
+synthetic input, every stage through libbi's HIP kernels:
+
+  1. RMSNorm      x bf16 [2048, 4096] -> y                      (bi_rmsnorm)
+  2. matmul       y [2048, 4096] x W bf16 [4096, 14336] -> C bf16 (bi_matmul)
+  3. prefill      one sequence's 512-token chunk at positions 3584..4095 of a
+                  paged cache (GQA 32/8, d=128): append + attention (bi_attn_prefill)
+  4. decode       64 sequences, lengths ~U{2048..4096} (one of length 4096),
+                  one new token each: append + split partials + fold (bi_attn_decode)
+
+The headline `value` is the invariant matmul's TFLOP/s (2*M*N*K over the
+matmul's average duration, from HIP events on the launch stream over the timed
+steps); RMSNorm and decode-attention GB/s and the prefill TFLOP/s are in
+`components`, each with its roofline fraction.  All inputs are resident in HBM
+before timing starts.  Also reported: the non-invariant comparators on the same
+inputs (cost of invariance), a bitwise invariance check, and the fp64 oracle
+timed on the host's cores on a bounded sample of the matmul.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+MFMA_BF16_PEAK = 2500.0   # TFLOP/s, dense bf16
+
+M, K, N = 2048, 4096, 14336
+H = 4096
+NQ, NKV, D = 32, 8, 128
+B_DEC, L_MAX = 64, 4096
+PREFILL_CHUNK = 512
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "invariant_bi_matmul_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    def __init__(self, seed: int = 0):
+        import numpy as np
+        import torch
+
+        import invariant_bi_matmul_amd as bi
+        import synth
+        self.bi, self.torch, self.np, self.synth = bi, torch, np, synth
+        dev = torch.device("cuda:0")
+        self.dev = dev
+
+        def to_dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+
+        self.to_dev = to_dev
+        # RMSNorm + matmul (host bits kept for the oracle sample)
+        self.x_bits, self.g_bits = synth.rmsnorm_inputs(M, H, seed=seed)
+        _, self.w_bits = synth.matmul_inputs(1, N, K, seed=seed)
+        self.x = to_dev(self.x_bits)
+        self.g = to_dev(self.g_bits)
+        self.w = to_dev(self.w_bits)
+        self.y = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+        self.c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        self.eps = float(np.float32(1e-6))
+        # attention: 64 decoding sequences + 1 sequence in chunked prefill
+        lens, self.probe = synth.ragged_lengths(B_DEC, L_MAX, seed=seed)
+        self.dec_lens = lens
+        self.pre_len = L_MAX
+        caps = lens + [self.pre_len]
+        pages = [(c + 15) // 16 for c in caps]
+        self.num_pages = sum(pages) + 3
+        perm = synth.stream(seed, "bench.pages").permutation(self.num_pages).astype(np.int32)
+        maxp = max(pages)
+        bt = np.full((len(caps), maxp), -1, dtype=np.int32)
+        cur = 0
+        for b, p in enumerate(pages):
+            bt[b, :p] = perm[cur:cur + p]
+            cur += p
+        self.bt_host = bt
+        self.bt_dec = torch.from_numpy(bt[:B_DEC].copy()).to(dev)
+        self.bt_pre = torch.from_numpy(bt[B_DEC:].copy()).to(dev)
+        shape = (self.num_pages, NKV, 16, D)
+        self.kc = synth.device_normal_bf16(shape, 0.0, 1.0, seed, "bench.kpool", dev)
+        self.vc = synth.device_normal_bf16(shape, 0.0, 1.0, seed, "bench.vpool", dev)
+        self.scale = float(np.float32(1.0 / np.sqrt(D)))
+        # decode inputs
+        self.q_dec = to_dev(synth.normal_bits((B_DEC, NQ, D), 0, 1, seed, "bench.qdec"))
+        self.k_dec = to_dev(synth.normal_bits((B_DEC, NKV, D), 0, 1, seed, "bench.kdec"))
+        self.v_dec = to_dev(synth.normal_bits((B_DEC, NKV, D), 0, 1, seed, "bench.vdec"))
+        self.kvl_dec = torch.tensor(lens, dtype=torch.int32, device=dev)
+        self.out_dec = torch.empty(B_DEC, NQ, D, dtype=torch.bfloat16, device=dev)
+        self.lse_dec = torch.empty(B_DEC, NQ, dtype=torch.float32, device=dev)
+        ash = bi.make_shape(B_DEC, NQ, NKV, D, maxp, self.num_pages, self.scale)
+        self.ws_bytes = bi.attn_workspace_bytes(ash, B_DEC, L_MAX)
+        self.ws = torch.empty(self.ws_bytes // 4 + 4, dtype=torch.float32, device=dev)
+        # prefill inputs: positions pre_len-512 .. pre_len-1
+        T = PREFILL_CHUNK
+        self.q_pre = to_dev(synth.normal_bits((T, NQ, D), 0, 1, seed, "bench.qpre"))
+        self.k_pre = to_dev(synth.normal_bits((T, NKV, D), 0, 1, seed, "bench.kpre"))
+        self.v_pre = to_dev(synth.normal_bits((T, NKV, D), 0, 1, seed, "bench.vpre"))
+        self.cu_pre = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        self.kvl_pre = torch.tensor([self.pre_len], dtype=torch.int32, device=dev)
+        self.out_pre = torch.empty(T, NQ, D, dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+
+    # -- the four stages ------------------------------------------------------
+    def rmsnorm(self):
+        self.bi.rmsnorm(self.x, self.g, self.eps, out=self.y)
+
+    def matmul(self):
+        self.bi.matmul(self.y, self.w, out=self.c)
+
+    def prefill(self):
+        self.bi.attn_prefill(self.q_pre, self.k_pre, self.v_pre, self.cu_pre, self.kvl_pre,
+                             self.bt_pre, self.kc, self.vc, self.scale, PREFILL_CHUNK,
+                             out=self.out_pre)
+
+    def decode(self):
+        self.bi.attn_decode(self.q_dec, self.k_dec, self.v_dec, self.kvl_dec, self.bt_dec,
+                            self.kc, self.vc, self.scale, L_MAX, workspace=self.ws,
+                            out=self.out_dec, lse=self.lse_dec)
+
+    STAGES = ("rmsnorm", "matmul", "prefill", "decode")
+
+    # -- algorithmic work ------------------------------------------------------
+    def work(self):
+        kv_tok = sum(self.dec_lens)
+        pos0 = self.pre_len - PREFILL_CHUNK
+        pre_pairs = sum(p + 1 for p in range(pos0, self.pre_len))  # (query, key) pairs
+        return {
+            # bytes: read x, write y (2 B each), gamma once
+            "rmsnorm": {"bytes": 2 * M * H * 2 + 2 * H},
+            "matmul": {"flops": 2.0 * M * N * K, "bytes": 2 * (M * K + K * N + M * N)},
+            # causal attention of 512 queries x 32 heads: QK^T and PV, 4*d flops per pair
+            "prefill": {"flops": 4.0 * D * NQ * pre_pairs},
+            # K and V of every cached position (8 kv heads, d=128, bf16) + q, out, new k/v
+            "decode": {"bytes": kv_tok * NKV * D * 2 * 2 + B_DEC * NQ * D * 2 * 2
+                       + B_DEC * NKV * D * 2 * 2},
+        }
+
+
+def time_steps(wl, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        for s in wl.STAGES:
+            getattr(wl, s)()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(wl.STAGES) + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        for j, s in enumerate(wl.STAGES):
+            getattr(wl, s)()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {s: 0.0 for s in wl.STAGES}
+    for i in range(steps):
+        for j, s in enumerate(wl.STAGES):
+            per[s] += ev[i][j].elapsed_time(ev[i][j + 1])
+    return wall, {s: per[s] / steps for s in wl.STAGES}  # ms
+
+
+def time_call(fn, reps=20, warmup=3):
+    import torch
+    for _ in range(warmup):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps  # ms
+
+
+def invariance_check(wl):
+    """Bitwise: matmul rows at M=8 vs M=2048; RMSNorm rows at 8 vs 2048 rows;
+    the probe sequence's decode row alone vs in the batch of 64."""
+    import torch
+    bi = wl.bi
+    res = {}
+    c8 = bi.matmul(wl.y[:8].contiguous(), wl.w)
+    res["matmul"] = bool(torch.equal(c8.view(torch.int16), wl.c[:8].view(torch.int16)))
+    y8 = bi.rmsnorm(wl.x[:8].contiguous(), wl.g, wl.eps)
+    res["rmsnorm"] = bool(torch.equal(y8.view(torch.int16), wl.y[:8].view(torch.int16)))
+    p = wl.probe
+    o1 = bi.attn_decode(wl.q_dec[p:p + 1].contiguous(), wl.k_dec[p:p + 1].contiguous(),
+                        wl.v_dec[p:p + 1].contiguous(), wl.kvl_dec[p:p + 1].contiguous(),
+                        wl.bt_dec[p:p + 1].contiguous(), wl.kc, wl.vc, wl.scale, L_MAX)
+    res["attn_decode"] = bool(torch.equal(o1[0].view(torch.int16), wl.out_dec[p].view(torch.int16)))
+    torch.cuda.synchronize()
+    return res
+
+
+def comparators(wl):
+    """Invariant kernel vs its non-invariant comparator on the same inputs (ms)."""
+    import torch
+    bi = wl.bi
+    out = {}
+    for m in (1, 16, 256, 2048):
+        a = wl.y[:m].contiguous()
+        ws = torch.empty(max(1, wl.bi.load().bix_matmul_workspace_bytes(m, N, K, 0)) // 4 + 4,
+                         dtype=torch.float32, device=wl.dev)
+        ti = time_call(lambda: bi.matmul(a, wl.w, out=wl.c[:m]))
+        tc = time_call(lambda: bi.bix_matmul_splitk(a, wl.w, out=wl.c[:m], workspace=ws))
+        out["matmul_M%d_N%d" % (m, N)] = {"invariant_ms": ti, "splitk_ms": tc,
+                                          "invariant_over_splitk": ti / tc}
+    for r in (1, 16, 2048):
+        xr = wl.x[:r].contiguous()
+        ws = torch.empty(r * 64, dtype=torch.float32, device=wl.dev)
+        yr = torch.empty_like(xr)
+        ti = time_call(lambda: bi.rmsnorm(xr, wl.g, wl.eps, out=yr))
+        tc = time_call(lambda: bi.bix_rmsnorm_splitrow(xr, wl.g, wl.eps, out=yr, workspace=ws))
+        out["rmsnorm_rows%d" % r] = {"invariant_ms": ti, "splitrow_ms": tc,
+                                     "invariant_over_splitrow": ti / tc}
+    for bsz in (1, 8, 64):
+        sl = slice(0, bsz)
+        args = (wl.q_dec[sl].contiguous(), wl.k_dec[sl].contiguous(), wl.v_dec[sl].contiguous(),
+                wl.kvl_dec[sl].contiguous(), wl.bt_dec[sl].contiguous(), wl.kc, wl.vc, wl.scale,
+                L_MAX)
+        o = torch.empty(bsz, NQ, D, dtype=torch.bfloat16, device=wl.dev)
+        ti = time_call(lambda: bi.attn_decode(*args, out=o))
+        tc = time_call(lambda: bi.bix_attn_decode_splitkv(*args, out=o))
+        out["decode_B%d_L%d" % (bsz, L_MAX)] = {"invariant_ms": ti, "splitkv_ms": tc,
+                                                "invariant_over_splitkv": ti / tc}
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(wl, target_s=10.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the step's matmul:
+    rows of A (the RMSNorm output) times the full W, timed on this host."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    a_bits = wl.y.detach().view(wl.torch.int16).cpu().numpy().view(np.uint16)
+    threads = oracle.default_threads()
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.matmul(a_bits, wl.w_bits, rows=range(rows), threads=threads)
+    dt = time.perf_counter() - t0
+    # scale the sample to about target_s seconds of CPU work
+    rows = int(min(M, max(16, rows * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.matmul(a_bits, wl.w_bits, rows=range(rows), threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d rows of the [%d,%d]x[%d,%d] matmul, fp64, %.1f s" %
+                      (rows, M, M, K, K, N, dt)}
+
+
+def traffic_for(kernel_file):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel_file)
+    if not rec or rec.get("source_sha") != source_sha(kernel_file, "common.h"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def calibrate_copy(nbytes=1 << 30):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparator timings and the invariance check")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    log("bench: generating inputs")
+    wl = Workload()
+    log("bench: warmup %d, timing %d steps" % (args.warmup, args.steps))
+    torch.cuda.synchronize()
+    wall, per = time_steps(wl, args.steps, args.warmup)
+    ms_step = wall * 1e3 / args.steps
+    w = wl.work()
+    mm_ms = per["matmul"]
+    tflops = w["matmul"]["flops"] / (mm_ms * 1e-3) / 1e12
+    comp = {
+        "rmsnorm": {"ms": per["rmsnorm"], "GB/s": w["rmsnorm"]["bytes"] / per["rmsnorm"] / 1e6},
+        "matmul": {"ms": mm_ms, "TFLOP/s": tflops},
+        "attn_prefill": {"ms": per["prefill"],
+                         "TFLOP/s": w["prefill"]["flops"] / per["prefill"] / 1e9},
+        "attn_decode": {"ms": per["decode"], "GB/s": w["decode"]["bytes"] / per["decode"] / 1e6},
+    }
+    comp["rmsnorm"]["hbm_frac"] = comp["rmsnorm"]["GB/s"] / HBM_PEAK_GBS
+    comp["matmul"]["mfma_frac"] = tflops / MFMA_BF16_PEAK
+    comp["attn_prefill"]["mfma_frac"] = comp["attn_prefill"]["TFLOP/s"] / MFMA_BF16_PEAK
+    comp["attn_decode"]["hbm_frac"] = comp["attn_decode"]["GB/s"] / HBM_PEAK_GBS
+    extras = {}
+    if not args.no_extras:
+        log("bench: invariance check and comparators")
+        extras["invariance_bitwise"] = invariance_check(wl)
+        extras["cost_of_invariance"] = comparators(wl)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: oracle on the host")
+        cpu = cpu_baseline(wl)
+    traffic = traffic_for("matmul.hip")
+    line = {
+        "metric": "invariant matmul TFLOP/s + RMSNorm/attn GB/s (% roofline), bitwise row-invariance",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Llama-8B-shaped tensors, random-init weights)",
+        "config": {"workload": "batch-invariant hot path step: RMSNorm [2048,4096] -> "
+                               "matmul [2048,4096]x[4096,14336] -> attention prefill chunk "
+                               "512 @ 4096 + decode B=64 ragged L<=4096, GQA 32/8, d=128, "
+                               "16-token pages",
+                   "M": M, "K": K, "N": N, "decode_batch": B_DEC, "max_kv_len": L_MAX,
+                   "prefill_chunk": PREFILL_CHUNK},
+        "roofline": {"bound": "mfma", "kernel": "bi_matmul_kernel", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK,
+                     "traffic": traffic},
+        "components": comp,
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

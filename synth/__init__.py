@@ -183,3 +183,16 @@ def attn_problem(lens: Sequence[int], n_q: int, n_kv: int, d: int, seed: int = 0
         ks.append(k)
         vs.append(v)
     return AttnProblem(list(lens), n_q, n_kv, d, qs, ks, vs)
+
+
+def device_normal_bf16(shape, mean: float, std: float, seed: int, tag: str, device="cuda"):
+    """Large N(mean, std) bf16 tensors drawn directly on the GPU with torch's
+    seeded Philox generator (used for the benchmark's key/value pool, where a
+    host-side draw would dominate set-up time).  Rounded to bf16 by torch's
+    round-to-nearest-even conversion."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed << 32) ^ zlib.crc32(tag.encode("utf-8")))
+    t = torch.empty(shape, dtype=torch.float32, device=device)
+    t.normal_(mean, std, generator=g)
+    return t.to(torch.bfloat16)
