@@ -7,30 +7,37 @@
 //     token's keys take the same path whether they arrived in this call or
 //     long ago;
 //   * fixed-size splits -- keys are cut at absolute multiples of 256.  The
-//     partial of one split for one query column is computed by ONE device
-//     function (split_partial), and partials are folded left in ascending
-//     split order by ONE device function (fold_step).  Prefill folds in
-//     registers; decode writes partials to a workspace and a second kernel
-//     folds them; both call the same functions with the same operands, so a
-//     token's output row has the same bits either way.
+//     partial of one split for one query column is computed by ONE pair of
+//     device functions (split_qk, then split_pv), and partials are folded left
+//     in ascending split order by ONE pair of device functions (fold_coef,
+//     fold_apply).  Prefill folds in registers; decode writes partials to a
+//     workspace and a second kernel folds them; both run the same functions on
+//     the same operand values, so a token's output row has the same bits
+//     either way.  Operands always come from LDS with the same layout; only
+//     how they get there differs: decode streams each wave's split through a
+//     wave-private ring of 4 chunk slots (RingSrc), prefill copies a whole
+//     split into LDS for the four waves of a workgroup to share (StagedSrc).
+//     Both copy with direct global->LDS loads whose page is wave-uniform.
 //
-// Work unit: one wave64 computes the partial of one split for a block of 16
-// query columns (GQA: the columns are (position, head-of-group) pairs sharing
-// one kv head) with v_mfma_f32_16x16x32_bf16:
-//   S^T = K Q^T   (A = 16 keys x 32 dims, B = Q^T in registers)
+// Work unit: one wave64 computes the partial of one split for NB blocks of 16
+// query columns (GQA: the columns of a block are (position, head-of-group)
+// pairs sharing one kv head) with v_mfma_f32_16x16x32_bf16:
+//   S^T = K Q^T   (A = 16 keys x 32 dims, B = Q^T held in registers)
 //   O^T = V^T P^T (A = 16 dims x 32 keys, B = P^T straight from registers)
 // Keys of a 32-key chunk are permuted onto MFMA rows so that each lane's
-// accumulator holds the 8 consecutive keys it needs as the P^T operand; V is
-// transposed in registers, lane r owning dims DB*r .. DB*r+DB-1 (DB = d/16).
-// Masked keys (beyond the query position) get logit -inf and weight exactly
-// 0, and their addresses are clamped to a written position, so they add
-// exact zeros; chunks wholly beyond every column's position are skipped,
-// which is therefore exact too.
+// accumulator holds the 8 consecutive keys it needs as the P^T operand; the
+// V^T operand is read from LDS with the transposing load ds_read_b64_tr_b16.
+// All 8 chunks of a split are always computed.  Keys beyond a column's
+// position get logit -inf and weight exactly 0, and their addresses are
+// clamped to the last written position, so they add exact zeros: a split's
+// bits do not depend on how far past the query the split's keys run.
 //
 // bix_attn_decode_splitkv_* is the comparator from the problem column of the
 // same row: the key range of each sequence is cut into a number of splits
 // chosen from the batch, so split boundaries move with the batch.
 #include <limits.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -60,139 +67,254 @@ __device__ __forceinline__ float lse_of(float m2, float l) { return (m2 + fast_l
 
 template <int D>
 struct KV {
-  static constexpr int DS = D / 32;  // 32-wide MFMA k-steps over the head dim
-  static constexpr int DB = D / 16;  // O^T row blocks; lane owns DB consecutive dims
+  static constexpr int DS = D / 32;    // 32-wide MFMA k-steps over the head dim
+  static constexpr int DB = D / 16;    // O^T row blocks; lane owns DB consecutive dims
+  static constexpr int ROWB = D * 2;   // bytes per key row
+  static constexpr int CPR = D / 8;    // 16-byte chunks per key row
+  using vrow = std::conditional_t<D == 128, u32x4, u32x2>;  // DB dims of one key
 };
 
-// Address of position `pos` of one sequence / kv head in a paged pool.
+// In-chunk key of the S^T A-operand row this lane loads for half h.
+__device__ __forceinline__ int okey_k(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Key rows in LDS are D*2 bytes; their 16-byte chunks are XOR-swizzled by key.
+// K: chunk c of key k sits at c ^ kswz(k), spreading the keys one S^T operand
+// read touches over distinct bank groups.  V: chunk c sits at c ^ vswz(k),
+// which moves the 32-byte column group a transposed read takes from four
+// consecutive keys into four different bank windows.
+__device__ __forceinline__ int kswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+__device__ __forceinline__ int vswz(int k) { return (k & 3) << 1; }
+
+// ---- operand source: keys and values of 32-key chunks held in LDS ---------------
+// load_k<C>(kb): kb[h][t] = K[32C+okey_k(h,r)][32t+8q .. +7] of the split
+// load_v<C>(va): va[i]    = V[32C+8q .. 32C+8q+7][16i+r] (one bf16x8 per lane),
+//                read with two transposing loads (ds_read_b64_tr_b16): within
+//                each 16-lane group, lane i' addresses key 8q+4hh+i'/4, dims
+//                16i+4(i'%4)..+3, and lane j receives dim 16i+j of the 4 keys.
+// step<IDX>() runs before chunk IDX (0..7: K chunks, 8..15: V chunks) so a
+// source that streams chunks can wait for / refill its buffers.
 template <int D>
-__device__ __forceinline__ const uint16_t* kv_row(const uint16_t* pool, const int32_t* bt_row,
-                                                  int nkv, int g, int pos) {
-  const int page = bt_row[pos >> 4];
-  return pool + ((((int64_t)page * nkv + g) << 4) + (pos & 15)) * D;
+__device__ __forceinline__ u32x4 lds_k_operand(const uint8_t* rows, int h, int t) {
+  const int lane = threadIdx.x & (kWave - 1), r = lane & 15, q = lane >> 4;
+  const int k = okey_k(h, r);
+  return *(const u32x4*)(rows + k * KV<D>::ROWB + (((4 * t + q) ^ kswz(k)) << 4));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 lds_v_operand(const uint8_t* rows, int i) {
+  const int lane = threadIdx.x & (kWave - 1), r = lane & 15, q = lane >> 4;
+  const int d = 16 * i + 4 * (r & 3);
+  s16x4 v[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int k = 8 * q + 4 * hh + (r >> 2);
+    const uint8_t* p = rows + k * KV<D>::ROWB + (((d >> 3) ^ vswz(k)) << 4) + (d & 7) * 2;
+    v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{(uint32_t)(uint16_t)v[0][0] | ((uint32_t)(uint16_t)v[0][1] << 16),
+                                          (uint32_t)(uint16_t)v[0][2] | ((uint32_t)(uint16_t)v[0][3] << 16),
+                                          (uint32_t)(uint16_t)v[1][0] | ((uint32_t)(uint16_t)v[1][1] << 16),
+                                          (uint32_t)(uint16_t)v[1][2] | ((uint32_t)(uint16_t)v[1][3] << 16)});
 }
 
-// Partial of keys key0 .. key0 + 32*nchunks - 1 for this wave's 16 columns.
-// Lane l (r = l%16, q = l/16) owns column r, whose query sits at position
-// pcol; key j is valid iff j <= pcol and j < key_end.  Addresses of keys at
-// or beyond `written` (a count of written positions) are clamped to
-// written-1.  Returns m (base-2 max logit, -inf if nothing valid), l, and o
-// (lane holds dims DB*(4q+t)+i in o[i][t]).
-template <int D>
-__device__ __forceinline__ void split_partial(const uint16_t* __restrict__ kc,
-                                              const uint16_t* __restrict__ vc,
-                                              const int32_t* __restrict__ bt_row, int nkv, int g,
-                                              int written, int key0, int nchunks, int key_end,
-                                              const bf16x8 (&qf)[KV<D>::DS], int pcol, float c2,
-                                              float& m_out, float& l_out,
-                                              f32x4 (&o)[KV<D>::DB]) {
-  constexpr int DS = KV<D>::DS, DB = KV<D>::DB;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int r = lane & 15, q = lane >> 4;
-  const int last = written - 1;
+// Page numbers of one 256-key split: pg[i] holds positions key0+16i..+15;
+// entries past the last written position use that position's page.  All
+// wave-uniform (scalar registers).
+struct SplitPages {
+  int pg[16];
+  int pg_last;
+  __device__ __forceinline__ void load(const int32_t* bt_row, int key0, int last) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      pg[i] = __builtin_amdgcn_readfirstlane(bt_row[min(key0 + 16 * i, last) >> 4]);
+    pg_last = __builtin_amdgcn_readfirstlane(bt_row[last >> 4]);
+  }
+};
 
-  float z[8][8];  // z[c][j]: key key0 + 32c + 8q + j, column r
-  // ---- S^T = K Q^T, chunk by chunk ----
+// One direct 1 KiB global->LDS load of the rows of keys kfirst..kfirst+KPI-1
+// of a split (KPI = 64 / chunks per row; all in the uniform page `page`) of
+// one kv head, swizzled for K or V, to LDS address lds_block.  Keys past
+// `last` read key `last` instead, so every value loaded is a written one.
+template <int D, bool IS_K>
+__device__ __forceinline__ void dma_block(const uint16_t* pool, int page, int nkv, int g, int key0,
+                                          int kfirst, int last, uint32_t lds_block) {
+  constexpr int CPR = KV<D>::CPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int kl = kfirst + lane / CPR, phys = lane % CPR;
+  const int logical = phys ^ (IS_K ? kswz(kl) : vswz(kl));
+  // past the last position the page is already last's (SplitPages), so only
+  // the slot needs clamping
+  const int slot = min(key0 + kl, last) & 15;
+  const uint16_t* base = pool + ((int64_t)page * nkv + g) * 16 * D;
+  lds_dma16_sv(base, (uint32_t)(slot * D + logical * 8) * 2, lds_block);
+}
+
+// A whole split staged in LDS by the workgroup (prefill): K and V rows of
+// keys 0..255 at kbase / vbase.
+template <int D>
+struct StagedSrc {
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  template <int IDX>
+  __device__ __forceinline__ void step() const {}
+  template <int C>
+  __device__ __forceinline__ u32x4 k(int h, int t) const {
+    return lds_k_operand<D>(kbase + 32 * C * KV<D>::ROWB, h, t);
+  }
+  template <int C>
+  __device__ __forceinline__ bf16x8 v(int i) const {
+    return lds_v_operand<D>(vbase + 32 * C * KV<D>::ROWB, i);
+  }
+};
+
+// A split streamed chunk by chunk through a wave-private ring of 4 LDS slots
+// (decode): the 16 chunk loads (K0..K7 then V0..V7) run three ahead of use.
+template <int D>
+struct RingSrc {
+  static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
+  static constexpr int LOADS = SLOT / 1024;          // 1 KiB loads per chunk
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const uint8_t* ring;  // 4 * SLOT bytes owned by this wave
+  SplitPages sp;
+  int nkv, g, key0, last;
+
+  template <int IDX>
+  __device__ __forceinline__ void issue() const {
+    constexpr int C = IDX & 7;
+    constexpr int KPI = kWave / KV<D>::CPR;
+    const uint32_t dst = (uint32_t)(uintptr_t)(ring + (IDX % 4) * SLOT);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    if (c < nchunks) {
-      f32x4 acc[2] = {f32x4{}, f32x4{}};
+    for (int n = 0; n < LOADS; ++n) {
+      const int kfirst = 32 * C + n * KPI;
+      dma_block<D, (IDX < 8)>(IDX < 8 ? kc : vc, sp.pg[(32 * C + n * KPI) >> 4], nkv, g, key0,
+                              kfirst, last, dst + (uint32_t)n * 1024);
+    }
+  }
+  __device__ __forceinline__ void prologue() const {
+    issue<0>();
+    issue<1>();
+    issue<2>();
+  }
+  template <int IDX>
+  __device__ __forceinline__ void step() const {
+    // chunks younger than IDX in flight: min(2, 15 - IDX)
+    wait_vmcnt_le<LOADS * (15 - IDX < 2 ? 15 - IDX : 2)>();
+    if constexpr (IDX + 3 < 16) issue<IDX + 3>();
+  }
+  template <int C>
+  __device__ __forceinline__ u32x4 k(int h, int t) const {
+    return lds_k_operand<D>(ring + (C % 4) * SLOT, h, t);
+  }
+  template <int C>
+  __device__ __forceinline__ bf16x8 v(int i) const {
+    return lds_v_operand<D>(ring + ((8 + C) % 4) * SLOT, i);
+  }
+};
+
+// ---- the split partial, in two phases -----------------------------------------
+// Lane l (r = l%16, q = l/16) owns column r of each of its NB blocks; block b's
+// query sits at position pcol[b]; key j is valid iff j <= pcol[b] and
+// j < key_end.  split_qk computes the logits, then per block m (base-2 max
+// logit, -inf if nothing valid) and l (sum of e = exp2(z - m) in fp32, 0 where
+// invalid), and leaves in p[b][c] the bf16 weights of keys key0+32c+8q+0..7.
+template <int D, int NB, class Src>
+__device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end,
+                                         const bf16x8 (&qf)[NB][KV<D>::DS], const int (&pcol)[NB],
+                                         float c2, u32x4 (&p)[NB][8], float (&m)[NB],
+                                         float (&l)[NB]) {
+  constexpr int DS = KV<D>::DS;
+  const int q = (threadIdx.x & (kWave - 1)) >> 4;
+  float z[NB][8][8];
+  auto chunk = [&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    src.template step<c>();
+    f32x4 acc[NB][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = key0 + 32 * c + 8 * (r >> 2) + 4 * h + (r & 3);
-        const uint16_t* kp = kv_row<D>(kc, bt_row, nkv, g, min(key, last)) + 8 * q;
+    for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = f32x4{};
 #pragma unroll
-        for (int t = 0; t < DS; ++t) {
-          const u32x4 a = *(const u32x4*)(kp + 32 * t);
-          acc[h] = mfma16(as_bf16x8(a), qf[t], acc[h]);
-        }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < DS; ++t) {
+        const bf16x8 a = as_bf16x8(src.template k<c>(h, t));
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][h] = mfma16(a, qf[b][t], acc[b][h]);
       }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = key0 + 32 * c + 8 * q + 4 * h + i;
-          const bool ok = key <= pcol && key < key_end;
-          z[c][4 * h + i] = ok ? acc[h][i] * c2 : -INFINITY;
+          const bool ok = key <= pcol[b] && key < key_end;
+          z[b][c][4 * h + i] = ok ? acc[b][h][i] * c2 : -INFINITY;
         }
-    } else {
+  };
+  chunk(std::integral_constant<int, 0>{});
+  chunk(std::integral_constant<int, 1>{});
+  chunk(std::integral_constant<int, 2>{});
+  chunk(std::integral_constant<int, 3>{});
+  chunk(std::integral_constant<int, 4>{});
+  chunk(std::integral_constant<int, 5>{});
+  chunk(std::integral_constant<int, 6>{});
+  chunk(std::integral_constant<int, 7>{});
+  // max, exponentials, sum: fixed order (chunks, then keys, then lanes)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) z[c][j] = -INFINITY;
-    }
-  }
-  // ---- max, exponentials, sum: fixed order (chunks, then keys, then lanes) ----
-  float m = -INFINITY;
+  for (int b = 0; b < NB; ++b) {
+    float mm = -INFINITY;
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, z[c][j]);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  float l = 0.0f;
+      for (int j = 0; j < 8; ++j) mm = fmaxf(mm, z[b][c][j]);
+    mm = fmaxf(mm, __shfl_xor(mm, 16));
+    mm = fmaxf(mm, __shfl_xor(mm, 32));
+    float ll = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 8; ++c) {
+      float e[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e = z[c][j] == -INFINITY ? 0.0f : fast_exp2(z[c][j] - m);
-      z[c][j] = e;
-      l = l + e;
-    }
-  l = l + __shfl_xor(l, 16);
-  l = l + __shfl_xor(l, 32);
-
-  // ---- O^T = V^T P^T ----
-#pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x4{};
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    if (c < nchunks) {
-      const u32x4 pw = u32x4{pack_bf16x2(z[c][0], z[c][1]), pack_bf16x2(z[c][2], z[c][3]),
-                             pack_bf16x2(z[c][4], z[c][5]), pack_bf16x2(z[c][6], z[c][7])};
-      const bf16x8 pf = as_bf16x8(pw);
-      if constexpr (DB == 8) {
-        u32x4 vr[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = key0 + 32 * c + 8 * q + j;
-          vr[j] = *(const u32x4*)(kv_row<D>(vc, bt_row, nkv, g, min(key, last)) + DB * r);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int w = i >> 1;
-          u32x4 va;
-          if (i & 1)
-            va = u32x4{pack_hi(vr[0][w], vr[1][w]), pack_hi(vr[2][w], vr[3][w]),
-                       pack_hi(vr[4][w], vr[5][w]), pack_hi(vr[6][w], vr[7][w])};
-          else
-            va = u32x4{pack_lo(vr[0][w], vr[1][w]), pack_lo(vr[2][w], vr[3][w]),
-                       pack_lo(vr[4][w], vr[5][w]), pack_lo(vr[6][w], vr[7][w])};
-          o[i] = mfma16(as_bf16x8(va), pf, o[i]);
-        }
-      } else {
-        static_assert(DB == 4, "head_dim 64 or 128");
-        u32x2 vr[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = key0 + 32 * c + 8 * q + j;
-          vr[j] = *(const u32x2*)(kv_row<D>(vc, bt_row, nkv, g, min(key, last)) + DB * r);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int w = i >> 1;
-          u32x4 va;
-          if (i & 1)
-            va = u32x4{pack_hi(vr[0][w], vr[1][w]), pack_hi(vr[2][w], vr[3][w]),
-                       pack_hi(vr[4][w], vr[5][w]), pack_hi(vr[6][w], vr[7][w])};
-          else
-            va = u32x4{pack_lo(vr[0][w], vr[1][w]), pack_lo(vr[2][w], vr[3][w]),
-                       pack_lo(vr[4][w], vr[5][w]), pack_lo(vr[6][w], vr[7][w])};
-          o[i] = mfma16(as_bf16x8(va), pf, o[i]);
-        }
+      for (int j = 0; j < 8; ++j) {
+        e[j] = z[b][c][j] == -INFINITY ? 0.0f : fast_exp2(z[b][c][j] - mm);
+        ll = ll + e[j];
       }
+      p[b][c] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                      pack_bf16x2(e[6], e[7])};
     }
+    ll = ll + __shfl_xor(ll, 16);
+    ll = ll + __shfl_xor(ll, 32);
+    m[b] = mm;
+    l[b] = ll;
   }
-  m_out = m;
-  l_out = l;
+}
+
+// O^T = V^T P^T over the split's chunks in ascending order; o[b][i][t] holds
+// dim 16i+4q+t of this lane's column in block b.
+template <int D, int NB, class Src>
+__device__ __forceinline__ void split_pv(const Src& src, const u32x4 (&p)[NB][8],
+                                         f32x4 (&o)[NB][KV<D>::DB]) {
+  constexpr int DB = KV<D>::DB;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[b][i] = f32x4{};
+  auto chunk = [&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    src.template step<8 + c>();
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      const bf16x8 va = src.template v<c>(i);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b][i] = mfma16(va, as_bf16x8(p[b][c]), o[b][i]);
+    }
+  };
+  chunk(std::integral_constant<int, 0>{});
+  chunk(std::integral_constant<int, 1>{});
+  chunk(std::integral_constant<int, 2>{});
+  chunk(std::integral_constant<int, 3>{});
+  chunk(std::integral_constant<int, 4>{});
+  chunk(std::integral_constant<int, 5>{});
+  chunk(std::integral_constant<int, 6>{});
+  chunk(std::integral_constant<int, 7>{});
 }
 
 // Q^T operand for d-step t: dims 32t + 8q .. +7 of this lane's query row.
@@ -202,7 +324,24 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, bool live, bf16x8 (
 #pragma unroll
   for (int t = 0; t < KV<D>::DS; ++t) {
     const u32x4 v = live ? *(const u32x4*)(qrow + 32 * t + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+    settle(v);  // the untracked LDS loads that follow must not be waited on for q
     qf[t] = as_bf16x8(v);
+  }
+}
+
+// Write one block's partial record (o[D], m, l) for a live column.
+template <int D>
+__device__ __forceinline__ void store_partial(float* rec, const f32x4 (&o)[KV<D>::DB], float m,
+                                              float l) {
+  constexpr int DB = KV<D>::DB;
+  const int qq = (threadIdx.x & (kWave - 1)) >> 4;
+#pragma unroll
+  for (int i = 0; i < DB; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rec[16 * i + 4 * qq + t] = o[i][t];
+  if (qq == 0) {
+    rec[D] = m;
+    rec[D + 1] = l;
   }
 }
 
@@ -249,9 +388,10 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
     const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
     int smax, float c2) {
-  constexpr int DB = KV<D>::DB;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][4 * RingSrc<D>::SLOT];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t u = (int64_t)blockIdx.x * 4 + wave;
   const int s = (int)(u % smax);
   const int64_t rest = u / smax;
   const int g = (int)(rest % nkv);
@@ -264,26 +404,18 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
   const int col = lane & 15;
   const bool live = col < group;
   const int hq = g * group + (live ? col : 0);
-  bf16x8 qf[KV<D>::DS];
-  load_q<D>(q + ((int64_t)b * nq + hq) * D, live, qf);
-  const int pcol = L - 1;
-  const int nch = min(8, (L - key0 + 31) / 32);
-  float m, l;
-  f32x4 o[DB];
-  split_partial<D>(kc, vc, bt + (int64_t)b * max_pages, nkv, g, L, key0, nch, INT_MAX, qf, pcol,
-                   c2, m, l, o);
-  if (live) {
-    float* rec = ws + (((int64_t)b * nq + hq) * smax + s) * (D + 2);
-    const int qq = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) rec[DB * (4 * qq + t) + i] = o[i][t];
-    if (qq == 0) {
-      rec[D] = m;
-      rec[D + 1] = l;
-    }
-  }
+  bf16x8 qf[1][KV<D>::DS];
+  load_q<D>(q + ((int64_t)b * nq + hq) * D, live, qf[0]);
+  const int pcol[1] = {L - 1};
+  RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1};
+  src.sp.load(bt + (int64_t)b * max_pages, key0, L - 1);
+  src.prologue();
+  u32x4 p[1][8];
+  float m[1], l[1];
+  f32x4 o[1][KV<D>::DB];
+  split_qk<D, 1>(src, key0, INT_MAX, qf, pcol, c2, p, m, l);
+  split_pv<D, 1>(src, p, o);
+  if (live) store_partial<D>(ws + (((int64_t)b * nq + hq) * smax + s) * (D + 2), o[0], m[0], l[0]);
 }
 
 // Fold the splits of one (sequence, q head) left in ascending order.
@@ -313,75 +445,135 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
 }
 
 // ---- prefill -----------------------------------------------------------------
-// Grid (query tiles, kv heads, sequences); 4 waves per workgroup, each wave a
-// block of 16/group positions x group heads.  Tiles run latest-first.
+// Grid (query tiles, kv heads, sequences); 4 waves per workgroup, each wave NB
+// blocks of 16/group positions x group heads.  Tiles run latest-first.  Each
+// 256-key split is copied into LDS (K, then V, by direct global->LDS loads)
+// and shared by the four waves: V(s) loads while K(s) is used, K(s+1) while
+// V(s) is used.
+constexpr int kPrefillNB = 1;
+
+// Copy the K or V rows of a whole 256-key split into LDS: thread t's load n
+// fills the 1 KiB block n*4 + t/64 (one page is 16 keys = 4 KiB at d=128,
+// 2 KiB at d=64, so every load stays within one page).
+template <int D, bool IS_K>
+__device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPages& sp, int nkv,
+                                            int g, int key0, int last, uint8_t* lds) {
+  constexpr int KPI = kWave / KV<D>::CPR;       // keys per 1 KiB load
+  constexpr int NLOAD = 256 / KPI / 4;          // loads per thread (4 waves)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool hi = ((wave * KPI) >> 4) != 0;     // the wave's keys start in the next page
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+#pragma unroll
+  for (int n = 0; n < NLOAD; ++n) {
+    const int pidx = (n * 4 * KPI) >> 4;        // compile-time after unrolling
+    const int page = (hi && pidx + 1 < 16) ? sp.pg[pidx + 1] : sp.pg[pidx];
+    const int kfirst = (n * 4 + wave) * KPI;
+    dma_block<D, IS_K>(pool, page, nkv, g, key0, kfirst, last,
+                       base + (uint32_t)kfirst * KV<D>::ROWB);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ bt,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nq, int nkv, int max_pages, float c2) {
-  constexpr int DB = KV<D>::DB;
+  constexpr int NB = kPrefillNB, DB = KV<D>::DB;
+  __shared__ __attribute__((aligned(1024))) uint8_t klds[256 * KV<D>::ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vlds[256 * KV<D>::ROWB];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.z, g = blockIdx.y;
   const int tile = (int)(gridDim.x - 1 - blockIdx.x);
   const int group = nq / nkv;
-  const int ppw = 16 / group;  // positions per wave
+  const int ppb = 16 / group;  // positions per block
+  const int per_wg = 4 * NB * ppb;
   const int tok0 = cu_q[b];
   const int nb = cu_q[b + 1] - tok0;
-  const int i0 = (tile * 4 + wave) * ppw;
-  if (i0 >= nb) return;
+  if (tile * per_wg >= nb) return;  // whole workgroup: no barrier reached
   const int L = kv_len[b];
   const int start = L - nb;
   const int col = lane & 15;
-  const int pi = i0 + col / group;
-  const bool live = pi < nb;
   const int hq = g * group + col % group;
-  const int64_t tok = tok0 + min(pi, nb - 1);
-  bf16x8 qf[KV<D>::DS];
-  load_q<D>(q + (tok * nq + hq) * D, live, qf);
-  const int pcol = live ? start + pi : -1;
-  const int pmax = start + min(i0 + ppw, nb) - 1;
-  const int32_t* bt_row = bt + (int64_t)b * max_pages;
-
-  float M = -INFINITY, Lsum = 0.0f;
-  f32x4 O[DB];
+  bf16x8 qf[NB][KV<D>::DS];
+  int pcol[NB];
+  int64_t tok[NB];
+  bool live[NB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) O[i] = f32x4{};
+  for (int bb = 0; bb < NB; ++bb) {
+    const int pi = tile * per_wg + (wave * NB + bb) * ppb + col / group;
+    live[bb] = pi < nb;
+    tok[bb] = tok0 + min(pi, nb - 1);
+    load_q<D>(q + (tok[bb] * nq + hq) * D, live[bb], qf[bb]);
+    pcol[bb] = live[bb] ? start + pi : -1;
+  }
+  const int pmax = start + min((tile + 1) * per_wg, nb) - 1;
   const int nsplit = pmax / kSplit + 1;
+  const int32_t* bt_row = bt + (int64_t)b * max_pages;
+  const StagedSrc<D> src{klds, vlds};
+
+  float M[NB], Lsum[NB];
+  f32x4 O[NB][DB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    M[bb] = -INFINITY;
+    Lsum[bb] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) O[bb][i] = f32x4{};
+  }
+  SplitPages pages;
+  pages.load(bt_row, 0, L - 1);
+  stage_split<D, true>(kc, pages, nkv, g, 0, L - 1, klds);
   for (int s = 0; s < nsplit; ++s) {
     const int key0 = s * kSplit;
-    const int nch = min(8, (pmax - key0 + 32) / 32);
-    float ms, ls;
-    f32x4 os[DB];
-    split_partial<D>(kc, vc, bt_row, nkv, g, L, key0, nch, INT_MAX, qf, pcol, c2, ms, ls, os);
-    if (key0 <= pcol) {
-      if (s == 0) {
-        M = ms;
-        Lsum = ls;
+    wait_vmcnt_le<0>();
+    __syncthreads();  // K(s) in LDS; every wave is done reading V(s-1)
+    stage_split<D, false>(vc, pages, nkv, g, key0, L - 1, vlds);
+    SplitPages next;  // the next split's pages, fetched while this one computes
+    if (s + 1 < nsplit) next.load(bt_row, key0 + kSplit, L - 1);
+    u32x4 p[NB][8];
+    float ms[NB], ls[NB];
+    split_qk<D, NB>(src, key0, INT_MAX, qf, pcol, c2, p, ms, ls);
+    wait_vmcnt_le<0>();
+    __syncthreads();  // V(s) in LDS; every wave is done reading K(s)
+    if (s + 1 < nsplit) {
+      pages = next;
+      stage_split<D, true>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds);
+    }
+    f32x4 os[NB][DB];
+    split_pv<D, NB>(src, p, os);
 #pragma unroll
-        for (int i = 0; i < DB; ++i) O[i] = os[i];
-      } else {
-        const FoldCoef f = fold_coef(M, ms);
-        Lsum = fold_apply(Lsum, ls, f);
+    for (int bb = 0; bb < NB; ++bb) {
+      if (key0 <= pcol[bb]) {
+        if (s == 0) {
+          M[bb] = ms[bb];
+          Lsum[bb] = ls[bb];
 #pragma unroll
-        for (int i = 0; i < DB; ++i)
+          for (int i = 0; i < DB; ++i) O[bb][i] = os[bb][i];
+        } else {
+          const FoldCoef f = fold_coef(M[bb], ms[bb]);
+          Lsum[bb] = fold_apply(Lsum[bb], ls[bb], f);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) O[i][t] = fold_apply(O[i][t], os[i][t], f);
-        M = f.m;
+          for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) O[bb][i][t] = fold_apply(O[bb][i][t], os[bb][i][t], f);
+          M[bb] = f.m;
+        }
       }
     }
   }
-  if (live) {
-    const int64_t orow = (tok * nq + hq) * D;
-    const int qq = lane >> 4;
+  const int qq = lane >> 4;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    if (!live[bb]) continue;
+    const int64_t orow = (tok[bb] * nq + hq) * D;
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        out[orow + DB * (4 * qq + t) + i] = (uint16_t)f32_to_bf16(O[i][t] / Lsum);
-    if (lse != nullptr && qq == 0) lse[tok * nq + hq] = lse_of(M, Lsum);
+        out[orow + 16 * i + 4 * qq + t] = (uint16_t)f32_to_bf16(O[bb][i][t] / Lsum[bb]);
+    if (lse != nullptr && qq == 0) lse[tok[bb] * nq + hq] = lse_of(M[bb], Lsum[bb]);
   }
 }
 
@@ -395,8 +587,10 @@ __global__ __launch_bounds__(256) void bix_attn_decode_splitkv_kernel(
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
     int nsplit, int split_len, float c2) {
   constexpr int DB = KV<D>::DB;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][4 * RingSrc<D>::SLOT];
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t u = (int64_t)blockIdx.x * 4 + wave;
   const int sp = (int)(u % nsplit);
   const int64_t rest = u / nsplit;
   const int g = (int)(rest % nkv);
@@ -410,43 +604,36 @@ __global__ __launch_bounds__(256) void bix_attn_decode_splitkv_kernel(
   const int col = lane & 15;
   const bool live = col < group;
   const int hq = g * group + (live ? col : 0);
-  bf16x8 qf[KV<D>::DS];
-  load_q<D>(q + ((int64_t)b * nq + hq) * D, live, qf);
+  bf16x8 qf[1][KV<D>::DS];
+  load_q<D>(q + ((int64_t)b * nq + hq) * D, live, qf[0]);
+  const int pcol[1] = {L - 1};
   float M = -INFINITY, Lsum = 0.0f;
   f32x4 O[DB];
   for (int key0 = k_begin; key0 < k_end; key0 += kSplit) {
-    const int nch = min(8, (k_end - key0 + 31) / 32);
-    float ms, ls;
-    f32x4 os[DB];
-    split_partial<D>(kc, vc, bt + (int64_t)b * max_pages, nkv, g, L, key0, nch, k_end, qf, L - 1,
-                     c2, ms, ls, os);
+    RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1};
+    src.sp.load(bt + (int64_t)b * max_pages, key0, L - 1);
+    src.prologue();
+    u32x4 p[1][8];
+    float ms[1], ls[1];
+    f32x4 os[1][DB];
+    split_qk<D, 1>(src, key0, k_end, qf, pcol, c2, p, ms, ls);
+    split_pv<D, 1>(src, p, os);
     if (key0 == k_begin) {
-      M = ms;
-      Lsum = ls;
+      M = ms[0];
+      Lsum = ls[0];
 #pragma unroll
-      for (int i = 0; i < DB; ++i) O[i] = os[i];
+      for (int i = 0; i < DB; ++i) O[i] = os[0][i];
     } else {
-      const FoldCoef f = fold_coef(M, ms);
-      Lsum = fold_apply(Lsum, ls, f);
+      const FoldCoef f = fold_coef(M, ms[0]);
+      Lsum = fold_apply(Lsum, ls[0], f);
 #pragma unroll
       for (int i = 0; i < DB; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) O[i][t] = fold_apply(O[i][t], os[i][t], f);
+        for (int t = 0; t < 4; ++t) O[i][t] = fold_apply(O[i][t], os[0][i][t], f);
       M = f.m;
     }
   }
-  if (live) {
-    float* rec = ws + (((int64_t)b * nq + hq) * nsplit + sp) * (D + 2);
-    const int qq = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) rec[DB * (4 * qq + t) + i] = O[i][t];
-    if (qq == 0) {
-      rec[D] = M;
-      rec[D + 1] = Lsum;
-    }
-  }
+  if (live) store_partial<D>(ws + (((int64_t)b * nq + hq) * nsplit + sp) * (D + 2), O, M, Lsum);
 }
 
 float base2_scale(float scale) { return scale * 1.44269504088896341f; }
@@ -472,8 +659,7 @@ hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* 
                                const int32_t* kv_len, const int32_t* bt, const void* kc,
                                const void* vc, void* out, float* lse, int max_q_per_seq,
                                hipStream_t st) {
-  const int ppw = 16 / (s.nq / s.nkv);
-  const int per_wg = 4 * ppw;
+  const int per_wg = 4 * kPrefillNB * (16 / (s.nq / s.nkv));
   const dim3 grid((unsigned)((max_q_per_seq + per_wg - 1) / per_wg), (unsigned)s.nkv,
                   (unsigned)s.B);
   const float c2 = base2_scale(s.scale);

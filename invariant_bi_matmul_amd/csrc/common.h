@@ -59,6 +59,54 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
+// address lds_base + 16*l (lds_base must be the same for the whole wave).  It
+// is written as inline asm so that the compiler does not track it: its own
+// conservative LDS-DMA tracking would wait for every load in flight before
+// each LDS read and serialise the pipeline.  The kernel instead waits on the
+// vector-memory counter explicitly (wait_vmcnt_le).  The instruction writes
+// no VGPR, so there is no register the compiler could reuse while it runs.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; no compiler code here reads it
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0v), "v"(gptr)
+               : "memory", "m0");
+}
+// The same load with a wave-uniform 64-bit base (scalar registers) plus a
+// 32-bit per-lane byte offset, so a lane's address costs one register.
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  // readfirstlane returns int: widen through uint32_t, never sign-extend
+  const uint64_t ub =
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0v), "v"(voff), "s"(ub)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Make the compiler wait for a value's load here (an empty asm that reads
+// it), before any untracked load is issued after it.
+template <class T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" : : "v"(x));
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (s_waitcnt with expcnt and lgkmcnt at their maxima, so only vmcnt waits).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (XCD = id % 8).
 // Renumber so that each XCD receives one contiguous range of logical ids,
 // which keeps neighbouring tiles in one XCD's L2.  A bijection for any count.

@@ -71,34 +71,6 @@ __device__ __forceinline__ int swz_a(int r) {
 // that the four k rows read by one transposed load land in distinct banks.
 __device__ __forceinline__ int swz_w(int k) { return (k & 3) << 1; }
 
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at LDS
-// address lds_base + 16*l (lds_base must be the same for the whole wave).  It
-// is written as inline asm so that the compiler does not track it: its own
-// conservative LDS-DMA tracking would wait for every load in flight before
-// each LDS read and serialise the pipeline.  The kernel instead waits on the
-// vector-memory counter explicitly (wait_vmcnt_le).  The instruction writes
-// no VGPR, so there is no register the compiler could reuse while it runs.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; no compiler code here reads it
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0v), "v"(gptr)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (s_waitcnt with expcnt and lgkmcnt at their maxima, so only vmcnt waits).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <class T, bool SPLIT>
 __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __restrict__ A,
                                                           const uint16_t* __restrict__ W,
