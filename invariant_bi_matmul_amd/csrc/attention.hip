@@ -166,12 +166,17 @@ struct StagedSrc {
   }
 };
 
-// A split streamed chunk by chunk through a wave-private ring of 4 LDS slots
-// (decode): the 16 chunk loads (K0..K7 then V0..V7) run three ahead of use.
+// A split streamed chunk by chunk through a wave-private ring of RING LDS
+// slots (decode): the 16 chunk loads (K0..K7 then V0..V7) run RING-1 ahead.
+constexpr int kRing = 5;  // 5 slots x 8 KiB x 4 waves = the 160 KiB of a CU at d=128
+
 template <int D>
 struct RingSrc {
+  static constexpr int RING = kRing;
   static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
   static constexpr int LOADS = SLOT / 1024;          // 1 KiB loads per chunk
+  static constexpr int AHEAD = RING - 1;             // chunks in flight
+  static_assert(LOADS * (AHEAD - 1) <= 63, "vmcnt range");
   const uint16_t* kc;
   const uint16_t* vc;
   const uint8_t* ring;  // 4 * SLOT bytes owned by this wave
@@ -182,7 +187,7 @@ struct RingSrc {
   __device__ __forceinline__ void issue() const {
     constexpr int C = IDX & 7;
     constexpr int KPI = kWave / KV<D>::CPR;
-    const uint32_t dst = (uint32_t)(uintptr_t)(ring + (IDX % 4) * SLOT);
+    const uint32_t dst = (uint32_t)(uintptr_t)(ring + (IDX % RING) * SLOT);
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
       const int kfirst = 32 * C + n * KPI;
@@ -190,24 +195,29 @@ struct RingSrc {
                               kfirst, last, dst + (uint32_t)n * 1024);
     }
   }
-  __device__ __forceinline__ void prologue() const {
-    issue<0>();
-    issue<1>();
-    issue<2>();
+  template <int IDX>
+  __device__ __forceinline__ void prologue_from() const {
+    if constexpr (IDX < AHEAD) {
+      issue<IDX>();
+      prologue_from<IDX + 1>();
+    }
   }
+  __device__ __forceinline__ void prologue() const { prologue_from<0>(); }
   template <int IDX>
   __device__ __forceinline__ void step() const {
-    // chunks younger than IDX in flight: min(2, 15 - IDX)
-    wait_vmcnt_le<LOADS * (15 - IDX < 2 ? 15 - IDX : 2)>();
-    if constexpr (IDX + 3 < 16) issue<IDX + 3>();
+    // chunks younger than IDX in flight: min(AHEAD - 1, 15 - IDX)
+    wait_vmcnt_le<LOADS * (15 - IDX < AHEAD - 1 ? 15 - IDX : AHEAD - 1)>();
+    // slot (IDX + AHEAD) % RING held chunk IDX - 1, whose reads this wave has
+    // already waited for
+    if constexpr (IDX + AHEAD < 16) issue<IDX + AHEAD>();
   }
   template <int C>
   __device__ __forceinline__ u32x4 k(int h, int t) const {
-    return lds_k_operand<D>(ring + (C % 4) * SLOT, h, t);
+    return lds_k_operand<D>(ring + (C % RING) * SLOT, h, t);
   }
   template <int C>
   __device__ __forceinline__ bf16x8 v(int i) const {
-    return lds_v_operand<D>(ring + ((8 + C) % 4) * SLOT, i);
+    return lds_v_operand<D>(ring + ((8 + C) % RING) * SLOT, i);
   }
 };
 
@@ -388,15 +398,17 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
     const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
     int smax, float c2) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][4 * RingSrc<D>::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][kRing * RingSrc<D>::SLOT];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // kv head fastest, then sequence, then split: the waves of a workgroup are
+  // kv heads of one (sequence, split), so they have work or none together
   const int64_t u = (int64_t)blockIdx.x * 4 + wave;
-  const int s = (int)(u % smax);
-  const int64_t rest = u / smax;
-  const int g = (int)(rest % nkv);
-  const int b = (int)(rest / nkv);
-  if (b >= B) return;
+  const int g = (int)(u % nkv);
+  const int64_t rest = u / nkv;
+  const int b = (int)(rest % B);
+  const int s = (int)(rest / B);
+  if (s >= smax) return;
   const int L = kv_len[b];
   const int key0 = s * kSplit;
   if (key0 >= L) return;
@@ -419,13 +431,16 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
 }
 
 // Fold the splits of one (sequence, q head) left in ascending order.
-// Thread d owns output dim d.  nsplit_of: splits actually present.
+// Thread d owns output dim d.  Partials are read in batches of 32 splits whose
+// loads are all issued before the batch is folded (the fold itself is the
+// same sequential left fold).
 template <int D>
 __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restrict__ ws,
                                                             const int32_t* __restrict__ kv_len,
                                                             uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, int nq,
                                                             int smax, int split_len) {
+  constexpr int BATCH = 32;
   const int64_t bh = blockIdx.x;
   const int b = (int)(bh / nq);
   const int d = threadIdx.x;
@@ -433,12 +448,25 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
   const int ns = min(smax, (L + split_len - 1) / split_len);
   const float* rec = ws + bh * smax * (D + 2);
   float m = rec[D], l = rec[D + 1], o = rec[d];
-  for (int s = 1; s < ns; ++s) {
-    const float* rs = rec + (int64_t)s * (D + 2);
-    const FoldCoef f = fold_coef(m, rs[D]);
-    l = fold_apply(l, rs[D + 1], f);
-    o = fold_apply(o, rs[d], f);
-    m = f.m;
+  for (int s0 = 1; s0 < ns; s0 += BATCH) {
+    float pm[BATCH], pl[BATCH], po[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = min(s0 + j, ns - 1);
+      const float* rs = rec + (int64_t)s * (D + 2);
+      pm[j] = rs[D];
+      pl[j] = rs[D + 1];
+      po[j] = rs[d];
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      if (s0 + j < ns) {
+        const FoldCoef f = fold_coef(m, pm[j]);
+        l = fold_apply(l, pl[j], f);
+        o = fold_apply(o, po[j], f);
+        m = f.m;
+      }
+    }
   }
   out[bh * D + d] = (uint16_t)f32_to_bf16(o / l);
   if (lse != nullptr && d == 0) lse[bh] = lse_of(m, l);
@@ -587,7 +615,7 @@ __global__ __launch_bounds__(256) void bix_attn_decode_splitkv_kernel(
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
     int nsplit, int split_len, float c2) {
   constexpr int DB = KV<D>::DB;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][4 * RingSrc<D>::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][kRing * RingSrc<D>::SLOT];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t u = (int64_t)blockIdx.x * 4 + wave;
