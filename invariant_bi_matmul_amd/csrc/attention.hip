@@ -15,7 +15,7 @@
 //     the same operand values, so a token's output row has the same bits
 //     either way.  Operands always come from LDS with the same layout; only
 //     how they get there differs: decode streams each wave's split through a
-//     wave-private ring of 4 chunk slots (RingSrc), prefill copies a whole
+//     wave-private ring of 5 chunk slots (RingSrc), prefill copies a whole
 //     split into LDS for the four waves of a workgroup to share (StagedSrc).
 //     Both copy with direct global->LDS loads whose page is wave-uniform.
 //
@@ -179,7 +179,7 @@ struct RingSrc {
   static_assert(LOADS * (AHEAD - 1) <= 63, "vmcnt range");
   const uint16_t* kc;
   const uint16_t* vc;
-  const uint8_t* ring;  // 4 * SLOT bytes owned by this wave
+  const uint8_t* ring;  // RING * SLOT bytes owned by this wave
   SplitPages sp;
   int nkv, g, key0, last;
 
@@ -207,9 +207,12 @@ struct RingSrc {
   __device__ __forceinline__ void step() const {
     // chunks younger than IDX in flight: min(AHEAD - 1, 15 - IDX)
     wait_vmcnt_le<LOADS * (15 - IDX < AHEAD - 1 ? 15 - IDX : AHEAD - 1)>();
-    // slot (IDX + AHEAD) % RING held chunk IDX - 1, whose reads this wave has
-    // already waited for
-    if constexpr (IDX + AHEAD < 16) issue<IDX + AHEAD>();
+    // slot (IDX + AHEAD) % RING held chunk IDX - 1: its reads must have
+    // returned before the refill can land
+    if constexpr (IDX + AHEAD < 16) {
+      lds_reads_done();
+      issue<IDX + AHEAD>();
+    }
   }
   template <int C>
   __device__ __forceinline__ u32x4 k(int h, int t) const {

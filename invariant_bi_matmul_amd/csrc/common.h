@@ -66,11 +66,15 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // each LDS read and serialise the pipeline.  The kernel instead waits on the
 // vector-memory counter explicitly (wait_vmcnt_le).  The instruction writes
 // no VGPR, so there is no register the compiler could reuse while it runs.
+// An LDS DMA that reads M0 must come at least one wait state after the SALU
+// write of M0 (the compiler's hazard recognizer cannot see inside the asm, so
+// the s_nop is written out here); without it the load may take the previous
+// M0 and land in another LDS block.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; no compiler code here reads it
 __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(m0v), "v"(gptr)
                : "memory", "m0");
@@ -84,7 +88,7 @@ __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, u
   const uint64_t ub =
       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(m0v), "v"(voff), "s"(ub)
                : "memory", "m0");
@@ -96,6 +100,13 @@ template <class T>
 __device__ __forceinline__ void settle(const T& x) {
   asm volatile("" : : "v"(x));
 }
+// Wait until every LDS read this wave has issued has returned.  A direct
+// global->LDS load writes LDS when its data arrives, with no ordering against
+// LDS reads still queued ahead of it, so a buffer may be refilled only after
+// this (or a workgroup barrier, whose fence waits the same way).  The memory
+// clobber keeps the compiler from moving LDS reads across it.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 

@@ -3,7 +3,7 @@
 // bi_matmul_kernel follows the MatMul row of the approach table in "Defeating
 // Nondeterminism in LLM Inference" (mobiles-han.blogspot.com summary): one
 // kernel configuration, compiled ahead, is used for every shape and batch
-// size.  Here that is one tile (BM x BN x BK = 128 x 128 x 64, four wave64s of
+// size.  Here that is one tile (BM x BN x BK = 256 x 128 x 64, eight wave64s of
 // 64 x 64 each), one MFMA instruction (v_mfma_f32_32x32x16_bf16), one k order
 // (k-tiles ascending, 16-wide MFMA steps ascending inside a tile) and no
 // split-K.  M only decides how many tiles exist; rows past M are computed from
@@ -17,9 +17,8 @@
 // the B operand, which needs 8 consecutive k per lane, is read with the
 // transposing LDS load ds_read_b64_tr_b16 (lane 4a+c of each 16-lane group
 // receives column c of the rows its group-mates a, a+4, a+8, a+12 address).
-// With 64 KiB of LDS per workgroup two workgroups share a CU, so the two waves
-// on each SIMD belong to different workgroups and their barriers do not line
-// up.
+// The LDS ring has three stages (144 KiB), so loads run two k-tiles ahead,
+// enough to cover the latency of reads that miss the caches.
 //
 // bix_matmul_* is the non-invariant comparator from the problem column of the
 // same row: split-K with a split count chosen from the grid size (so from M),
@@ -56,7 +55,7 @@ struct MMTile {
 };
 
 // The one configuration.
-using Tile = MMTile<128, 128, 64, 2, 2, 2, true>;
+using Tile = MMTile<256, 128, 64, 4, 2, 3, true>;
 
 // A in LDS: [BM rows][BK/8 chunks of 16 B]; chunk c of row r sits at
 // c ^ swz_a(r), chosen so that the 8 rows an MFMA operand read touches per
