@@ -96,7 +96,8 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t r
  * One compiled tile and one bf16 MFMA instruction for every m, n, k; each
  * element's k-loop runs in one fixed order; no split-K.  The bf16 result is
  * exactly the round-to-nearest-even of the fp32 result.
- * Requires k % 64 == 0, n % 8 == 0 (else BI_ERR_UNSUPPORTED).
+ * Requires k % 64 == 0, n % 8 == 0, k <= 2^22 and n <= 2^24 (else
+ * BI_ERR_UNSUPPORTED).
  */
 int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
               void* stream);

@@ -120,6 +120,8 @@ static int check_matmul(const void* a, const void* w, void* c, int c_dtype, int6
   if (c_dtype != BI_DTYPE_BF16 && c_dtype != BI_DTYPE_F32) return BI_ERR_INVALID_SHAPE;
   if (k % bi::kMatmulBK != 0 || n % 8 != 0) return BI_ERR_UNSUPPORTED;
   if (m > 0x7fffffff || n > 0x7fffffff || k > 0x7fffffff) return BI_ERR_UNSUPPORTED;
+  // per-thread load offsets inside a 256-row / 64-k-row tile are 32-bit
+  if (k > (int64_t)1 << 22 || n > (int64_t)1 << 24) return BI_ERR_UNSUPPORTED;
   if (m == 0 || n == 0) return -1;
   if (((m + 255) / 256) * ((n + 255) / 256) > kMaxGridX) return BI_ERR_UNSUPPORTED;
   if (c == nullptr || (k > 0 && (a == nullptr || w == nullptr))) return BI_ERR_NULL_POINTER;

@@ -77,13 +77,25 @@ struct KV {
 // In-chunk key of the S^T A-operand row this lane loads for half h.
 __device__ __forceinline__ int okey_k(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Key rows in LDS are D*2 bytes; their 16-byte chunks are XOR-swizzled by key.
-// K: chunk c of key k sits at c ^ kswz(k), spreading the keys one S^T operand
-// read touches over distinct bank groups.  V: chunk c sits at c ^ vswz(k),
-// which moves the 32-byte column group a transposed read takes from four
-// consecutive keys into four different bank windows.
-__device__ __forceinline__ int kswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
-__device__ __forceinline__ int vswz(int k) { return (k & 3) << 1; }
+// Key rows in LDS are D*2 bytes; their 16-byte chunks are XOR-swizzled by key
+// (k = key index within a 32-key chunk).  The LDS has 64 banks of 4 bytes and
+// serves 16 lanes of a 16-byte read, or 32 lanes of an 8-byte read, per clock.
+// K: chunk c of key k sits at c ^ kswz(k).  One clock of an S^T operand read
+// covers 16 keys that differ in bits 0, 1, 3, 4 of k; kswz maps them to 16
+// distinct 16-byte slots of the 256-byte bank row (d=128), or to 8 distinct
+// slots in each half for the two keys sharing a bank row (d=64).
+// V: chunk c sits at c ^ vswz(k).  One clock of a transposed read covers 8
+// keys (bits 0, 1, 3) x 32 bytes; vswz gives each key a distinct 32-byte slot.
+template <int D>
+__device__ __forceinline__ int kswz(int k) {
+  if constexpr (D == 128) return (k & 3) | (((k >> 3) & 3) << 2);
+  else return ((k >> 1) & 1) | (((k >> 3) & 3) << 1);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int k) {
+  if constexpr (D == 128) return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
+  else return (((k >> 1) & 1) | (((k >> 3) & 1) << 1)) << 1;
+}
 
 // ---- operand source: keys and values of 32-key chunks held in LDS ---------------
 // load_k<C>(kb): kb[h][t] = K[32C+okey_k(h,r)][32t+8q .. +7] of the split
@@ -97,7 +109,7 @@ template <int D>
 __device__ __forceinline__ u32x4 lds_k_operand(const uint8_t* rows, int h, int t) {
   const int lane = threadIdx.x & (kWave - 1), r = lane & 15, q = lane >> 4;
   const int k = okey_k(h, r);
-  return *(const u32x4*)(rows + k * KV<D>::ROWB + (((4 * t + q) ^ kswz(k)) << 4));
+  return *(const u32x4*)(rows + k * KV<D>::ROWB + (((4 * t + q) ^ kswz<D>(k)) << 4));
 }
 template <int D>
 __device__ __forceinline__ bf16x8 lds_v_operand(const uint8_t* rows, int i) {
@@ -107,7 +119,7 @@ __device__ __forceinline__ bf16x8 lds_v_operand(const uint8_t* rows, int i) {
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
     const int k = 8 * q + 4 * hh + (r >> 2);
-    const uint8_t* p = rows + k * KV<D>::ROWB + (((d >> 3) ^ vswz(k)) << 4) + (d & 7) * 2;
+    const uint8_t* p = rows + k * KV<D>::ROWB + (((d >> 3) ^ vswz<D>(k)) << 4) + (d & 7) * 2;
     v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   }
   return __builtin_bit_cast(bf16x8, u32x4{(uint32_t)(uint16_t)v[0][0] | ((uint32_t)(uint16_t)v[0][1] << 16),
@@ -140,7 +152,7 @@ __device__ __forceinline__ void dma_block(const uint16_t* pool, int page, int nk
   constexpr int CPR = KV<D>::CPR;
   const int lane = threadIdx.x & (kWave - 1);
   const int kl = kfirst + lane / CPR, phys = lane % CPR;
-  const int logical = phys ^ (IS_K ? kswz(kl) : vswz(kl));
+  const int logical = phys ^ (IS_K ? kswz<D>(kl) : vswz<D>(kl));
   // past the last position the page is already last's (SplitPages), so only
   // the slot needs clamping
   const int slot = min(key0 + kl, last) & 15;
