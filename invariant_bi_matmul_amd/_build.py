@@ -1,7 +1,8 @@
 """Build libbi.so (the C-ABI HIP library) for gfx950 with hipcc.
 
 One fixed flag set for every kernel: -O3, no fast-math, -ffp-contract=off
-(a*b+c stays a rounded multiply then a rounded add), packed-fp32 ops off.
+(a*b+c stays a rounded multiply then a rounded add), packed-fp32 ops off,
+MFMA results kept in ordinary VGPRs.
 Run as ``python -m invariant_bi_matmul_amd._build``; ``__graft_entry__.build()``
 calls :func:`build`.
 """
@@ -26,6 +27,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the softmax and fold read them with VALU,
+    # and accumulation registers would need a copy per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -122,10 +122,7 @@ __device__ __forceinline__ bf16x8 lds_v_operand(const uint8_t* rows, int i) {
     const uint8_t* p = rows + k * KV<D>::ROWB + (((d >> 3) ^ vswz<D>(k)) << 4) + (d & 7) * 2;
     v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
   }
-  return __builtin_bit_cast(bf16x8, u32x4{(uint32_t)(uint16_t)v[0][0] | ((uint32_t)(uint16_t)v[0][1] << 16),
-                                          (uint32_t)(uint16_t)v[0][2] | ((uint32_t)(uint16_t)v[0][3] << 16),
-                                          (uint32_t)(uint16_t)v[1][0] | ((uint32_t)(uint16_t)v[1][1] << 16),
-                                          (uint32_t)(uint16_t)v[1][2] | ((uint32_t)(uint16_t)v[1][3] << 16)});
+  return join_tr(v[0], v[1]);
 }
 
 // Page numbers of one 256-key split: pg[i] holds positions key0+16i..+15;
@@ -242,8 +239,10 @@ struct RingSrc {
 // j < key_end.  split_qk computes the logits, then per block m (base-2 max
 // logit, -inf if nothing valid) and l (sum of e = exp2(z - m) in fp32, 0 where
 // invalid), and leaves in p[b][c] the bf16 weights of keys key0+32c+8q+0..7.
+// pmin (wave-uniform) is at most the position of every column whose result is
+// used: a chunk whose last key is <= pmin and < key_end needs no masking.
 template <int D, int NB, class Src>
-__device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end,
+__device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, int pmin,
                                          const bf16x8 (&qf)[NB][KV<D>::DS], const int (&pcol)[NB],
                                          float c2, u32x4 (&p)[NB][8], float (&m)[NB],
                                          float (&l)[NB]) {
@@ -264,16 +263,26 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end,
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[b][h] = mfma16(a, qf[b][t], acc[b][h]);
       }
+    const int last = key0 + 32 * c + 31;
+    if (last <= pmin && last < key_end) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 32 * c + 8 * q + 4 * h + i;
-          const bool ok = key <= pcol[b] && key < key_end;
-          z[b][c][4 * h + i] = ok ? acc[b][h][i] * c2 : -INFINITY;
-        }
+          for (int i = 0; i < 4; ++i) z[b][c][4 * h + i] = acc[b][h][i] * c2;
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + 32 * c + 8 * q + 4 * h + i;
+            const bool ok = key <= pcol[b] && key < key_end;
+            z[b][c][4 * h + i] = ok ? acc[b][h][i] * c2 : -INFINITY;
+          }
+    }
   };
   chunk(std::integral_constant<int, 0>{});
   chunk(std::integral_constant<int, 1>{});
@@ -293,13 +302,15 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end,
       for (int j = 0; j < 8; ++j) mm = fmaxf(mm, z[b][c][j]);
     mm = fmaxf(mm, __shfl_xor(mm, 16));
     mm = fmaxf(mm, __shfl_xor(mm, 32));
+    // with no valid key every z is -inf; subtracting 0 keeps exp2(-inf) = 0
+    const float ms = mm == -INFINITY ? 0.0f : mm;
     float ll = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        e[j] = z[b][c][j] == -INFINITY ? 0.0f : fast_exp2(z[b][c][j] - mm);
+        e[j] = fast_exp2(z[b][c][j] - ms);
         ll = ll + e[j];
       }
       p[b][c] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
@@ -440,7 +451,7 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
   u32x4 p[1][8];
   float m[1], l[1];
   f32x4 o[1][KV<D>::DB];
-  split_qk<D, 1>(src, key0, INT_MAX, qf, pcol, c2, p, m, l);
+  split_qk<D, 1>(src, key0, INT_MAX, L - 1, qf, pcol, c2, p, m, l);
   split_pv<D, 1>(src, p, o);
   if (live) store_partial<D>(ws + (((int64_t)b * nq + hq) * smax + s) * (D + 2), o[0], m[0], l[0]);
 }
@@ -552,6 +563,9 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     pcol[bb] = live[bb] ? start + pi : -1;
   }
   const int pmax = start + min((tile + 1) * per_wg, nb) - 1;
+  // the wave's columns are consecutive positions from its first one on; lanes
+  // past the chunk's end are never stored or folded
+  const int pmin = start + tile * per_wg + wave * NB * ppb;
   const int nsplit = pmax / kSplit + 1;
   const int32_t* bt_row = bt + (int64_t)b * max_pages;
   const StagedSrc<D> src{klds, vlds};
@@ -577,7 +591,7 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     if (s + 1 < nsplit) next.load(bt_row, key0 + kSplit, L - 1);
     u32x4 p[NB][8];
     float ms[NB], ls[NB];
-    split_qk<D, NB>(src, key0, INT_MAX, qf, pcol, c2, p, ms, ls);
+    split_qk<D, NB>(src, key0, INT_MAX, pmin, qf, pcol, c2, p, ms, ls);
     wait_vmcnt_le<0>();
     __syncthreads();  // V(s) in LDS; every wave is done reading K(s)
     if (s + 1 < nsplit) {
@@ -659,7 +673,7 @@ __global__ __launch_bounds__(256) void bix_attn_decode_splitkv_kernel(
     u32x4 p[1][8];
     float ms[1], ls[1];
     f32x4 os[1][DB];
-    split_qk<D, 1>(src, key0, k_end, qf, pcol, c2, p, ms, ls);
+    split_qk<D, 1>(src, key0, k_end, L - 1, qf, pcol, c2, p, ms, ls);
     split_pv<D, 1>(src, p, os);
     if (key0 == k_begin) {
       M = ms[0];

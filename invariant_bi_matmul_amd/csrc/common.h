@@ -3,8 +3,8 @@
 // Numerics policy for every kernel of the library: built with
 // -ffp-contract=off and without fast-math, so a*b+c is always a rounded
 // multiply followed by a rounded add unless a kernel asks for fmaf.  bf16
-// results are rounded to nearest even by f32_to_bf16 below, the one
-// conversion used everywhere.
+// results are rounded to nearest even by pack_bf16x2 / f32_to_bf16 below, the
+// one conversion used everywhere.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,16 +24,18 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
+// Two floats -> two bf16 (lo in bits 0..15), round to nearest even; a NaN
+// becomes the quiet NaN with the same sign and top payload bits
+// ((bits >> 16) | 0x40); denormals are rounded, not flushed.  gfx950's
+// v_cvt_pk_bf16_f32 implements exactly this rule (checked against the
+// integer formulation over every upper half with boundary lower halves and
+// 4M random patterns), two values per instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.0f) & 0xffffu; }
 
 // Low halves / high halves of two packed bf16 pairs: (lo16(a), lo16(b)) etc.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
@@ -109,6 +111,12 @@ __device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmc
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Two 4 x 16-bit transposed-read results as one 8 x bf16 MFMA operand
+// (element 0 of `a` in bits 0..15 of the first dword).
+__device__ __forceinline__ bf16x8 join_tr(s16x4 a, s16x4 b) {
+  const u32x2 x = __builtin_bit_cast(u32x2, a), y = __builtin_bit_cast(u32x2, b);
+  return as_bf16x8(u32x4{x[0], x[1], y[0], y[1]});
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (s_waitcnt with expcnt and lgkmcnt at their maxima, so only vmcnt waits).

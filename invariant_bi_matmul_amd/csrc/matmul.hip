@@ -179,11 +179,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
       for (int h = 0; h < 2; ++h)
         v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(S + wo[ni] + (16 * kk + 4 * h) * T::W_ROW));
-      const u32x4 u = u32x4{(uint32_t)(uint16_t)v[0][0] | ((uint32_t)(uint16_t)v[0][1] << 16),
-                            (uint32_t)(uint16_t)v[0][2] | ((uint32_t)(uint16_t)v[0][3] << 16),
-                            (uint32_t)(uint16_t)v[1][0] | ((uint32_t)(uint16_t)v[1][1] << 16),
-                            (uint32_t)(uint16_t)v[1][2] | ((uint32_t)(uint16_t)v[1][3] << 16)};
-      bw[ni] = as_bf16x8(u);
+      bw[ni] = join_tr(v[0], v[1]);
     }
   };
 
