@@ -139,6 +139,20 @@ struct SplitPages {
   }
 };
 
+// Byte offset, inside one (page, kv head) block, of the 16-byte chunk a lane
+// of a direct load fetches for split key kl = kfirst + lane/CPR when no
+// clamping is needed: row kl mod 16, logical chunk phys ^ swz(kl).  Only kl
+// mod 32 matters, so a load's offsets depend on kfirst mod 32 alone and can be
+// computed once per kernel.
+template <int D, bool IS_K>
+__device__ __forceinline__ uint32_t dma_lane_off(int kfirst) {
+  constexpr int CPR = KV<D>::CPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int kl = kfirst + lane / CPR, phys = lane % CPR;
+  const int logical = phys ^ (IS_K ? kswz<D>(kl) : vswz<D>(kl));
+  return (uint32_t)(((kl & 15) * D + logical * 8) * 2);
+}
+
 // One direct 1 KiB global->LDS load of the rows of keys kfirst..kfirst+KPI-1
 // of a split (KPI = 64 / chunks per row; all in the uniform page `page`) of
 // one kv head, swizzled for K or V, to LDS address lds_block.  Keys past
@@ -179,6 +193,22 @@ struct StagedSrc {
 // slots (decode): the 16 chunk loads (K0..K7 then V0..V7) run RING-1 ahead.
 constexpr int kRing = 5;  // 5 slots x 8 KiB x 4 waves = the 160 KiB of a CU at d=128
 
+// Per-lane offsets of the loads of one 32-key chunk (load n covers keys
+// 32C + n*KPI.., the same offsets for every chunk C).
+template <int D>
+struct ChunkLaneOffs {
+  static constexpr int LOADS = 32 * KV<D>::ROWB / 1024;
+  uint32_t k[LOADS], v[LOADS];
+  __device__ __forceinline__ void init() {
+    constexpr int KPI = kWave / KV<D>::CPR;
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) {
+      k[n] = dma_lane_off<D, true>(n * KPI);
+      v[n] = dma_lane_off<D, false>(n * KPI);
+    }
+  }
+};
+
 template <int D>
 struct RingSrc {
   static constexpr int RING = kRing;
@@ -191,12 +221,22 @@ struct RingSrc {
   const uint8_t* ring;  // RING * SLOT bytes owned by this wave
   SplitPages sp;
   int nkv, g, key0, last;
+  const ChunkLaneOffs<D>* offs;  // used when the whole split is written (no clamping)
 
   template <int IDX>
   __device__ __forceinline__ void issue() const {
     constexpr int C = IDX & 7;
     constexpr int KPI = kWave / KV<D>::CPR;
     const uint32_t dst = (uint32_t)(uintptr_t)(ring + (IDX % RING) * SLOT);
+    if (key0 + kSplit - 1 <= last) {
+      const int64_t head = (int64_t)g * 16 * D, stride = (int64_t)nkv * 16 * D;
+      const uint16_t* pool = IDX < 8 ? kc : vc;
+#pragma unroll
+      for (int n = 0; n < LOADS; ++n)
+        lds_dma16_sv(pool + head + sp.pg[(32 * C + n * KPI) >> 4] * stride,
+                     IDX < 8 ? offs->k[n] : offs->v[n], dst + (uint32_t)n * 1024);
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
       const int kfirst = 32 * C + n * KPI;
@@ -241,58 +281,81 @@ struct RingSrc {
 // invalid), and leaves in p[b][c] the bf16 weights of keys key0+32c+8q+0..7.
 // pmin (wave-uniform) is at most the position of every column whose result is
 // used: a chunk whose last key is <= pmin and < key_end needs no masking.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// LDS operand reads are issued this many MFMA operands ahead of their use, so
+// their latency hides behind the MFMAs in between (one wave per SIMD: nothing
+// else would hide it).
+constexpr int kOperandsAhead = 4;
+
 template <int D, int NB, class Src>
 __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, int pmin,
                                          const bf16x8 (&qf)[NB][KV<D>::DS], const int (&pcol)[NB],
                                          float c2, u32x4 (&p)[NB][8], float (&m)[NB],
                                          float (&l)[NB]) {
   constexpr int DS = KV<D>::DS;
+  constexpr int OPC = 2 * DS;      // K operands per 32-key chunk: (half h, d-step t)
+  constexpr int NOP = 8 * OPC;
+  constexpr int PD = kOperandsAhead;
   const int q = (threadIdx.x & (kWave - 1)) >> 4;
   float z[NB][8][8];
-  auto chunk = [&](auto cc) {
-    constexpr int c = decltype(cc)::value;
-    src.template step<c>();
-    f32x4 acc[NB][2];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = f32x4{};
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int t = 0; t < DS; ++t) {
-        const bf16x8 a = as_bf16x8(src.template k<c>(h, t));
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b][h] = mfma16(a, qf[b][t], acc[b][h]);
-      }
-    const int last = key0 + 32 * c + 31;
-    if (last <= pmin && last < key_end) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) z[b][c][4 * h + i] = acc[b][h][i] * c2;
-    } else {
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 32 * c + 8 * q + 4 * h + i;
-            const bool ok = key <= pcol[b] && key < key_end;
-            z[b][c][4 * h + i] = ok ? acc[b][h][i] * c2 : -INFINITY;
-          }
-    }
+  u32x4 buf[PD];
+  // operand o = (chunk c, half h, d-step t); a chunk's first read waits for
+  // (and lets the source refill around) that chunk
+  auto read = [&](auto oc) {
+    constexpr int o = decltype(oc)::value;
+    constexpr int c = o / OPC, h = (o % OPC) / DS, t = o % DS;
+    if constexpr (o % OPC == 0) src.template step<c>();
+    buf[o % PD] = src.template k<c>(h, t);
   };
-  chunk(std::integral_constant<int, 0>{});
-  chunk(std::integral_constant<int, 1>{});
-  chunk(std::integral_constant<int, 2>{});
-  chunk(std::integral_constant<int, 3>{});
-  chunk(std::integral_constant<int, 4>{});
-  chunk(std::integral_constant<int, 5>{});
-  chunk(std::integral_constant<int, 6>{});
-  chunk(std::integral_constant<int, 7>{});
-  // max, exponentials, sum: fixed order (chunks, then keys, then lanes)
+  static_for<0, PD>(read);
+  f32x4 acc[NB][2];
+  static_for<0, NOP>([&](auto oc) {
+    constexpr int o = decltype(oc)::value;
+    constexpr int c = o / OPC, h = (o % OPC) / DS, t = o % DS;
+    if constexpr (o % OPC == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = f32x4{};
+    }
+    const bf16x8 a = as_bf16x8(buf[o % PD]);
+    if constexpr (o + PD < NOP) read(std::integral_constant<int, o + PD>{});
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b][h] = mfma16(a, qf[b][t], acc[b][h]);
+    if constexpr (o % OPC == OPC - 1) {
+      // raw dot products; -inf marks an invalid key
+      const int last = key0 + 32 * c + 31;
+      if (last <= pmin && last < key_end) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[b][c][4 * hh + i] = acc[b][hh][i];
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 32 * c + 8 * q + 4 * hh + i;
+              const bool ok = key <= pcol[b] && key < key_end;
+              z[b][c][4 * hh + i] = ok ? acc[b][hh][i] : -INFINITY;
+            }
+      }
+    }
+  });
+  // max, exponentials, sum: fixed order (chunks, then keys, then lanes).
+  // The base-2 logit of a key is s*c2 for its dot product s.  Rounding is
+  // monotone, so the largest rounded logit is round(max s * c2): the max is
+  // taken over the raw dot products and scaled once.  Each exponent is
+  // exp2(s*c2 - m) with s*c2 - m rounded once (fma).
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     float mm = -INFINITY;
@@ -302,7 +365,8 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
       for (int j = 0; j < 8; ++j) mm = fmaxf(mm, z[b][c][j]);
     mm = fmaxf(mm, __shfl_xor(mm, 16));
     mm = fmaxf(mm, __shfl_xor(mm, 32));
-    // with no valid key every z is -inf; subtracting 0 keeps exp2(-inf) = 0
+    mm = mm * c2;
+    // with no valid key every s is -inf; subtracting 0 keeps exp2(-inf) = 0
     const float ms = mm == -INFINITY ? 0.0f : mm;
     float ll = 0.0f;
 #pragma unroll
@@ -310,7 +374,7 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
       float e[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        e[j] = fast_exp2(z[b][c][j] - ms);
+        e[j] = fast_exp2(fmaf(z[b][c][j], c2, -ms));
         ll = ll + e[j];
       }
       p[b][c] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
@@ -329,28 +393,28 @@ template <int D, int NB, class Src>
 __device__ __forceinline__ void split_pv(const Src& src, const u32x4 (&p)[NB][8],
                                          f32x4 (&o)[NB][KV<D>::DB]) {
   constexpr int DB = KV<D>::DB;
+  constexpr int NOP = 8 * DB;      // V operands: (chunk c, dim block i)
+  constexpr int PD = kOperandsAhead;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[b][i] = f32x4{};
-  auto chunk = [&](auto cc) {
-    constexpr int c = decltype(cc)::value;
-    src.template step<8 + c>();
-#pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      const bf16x8 va = src.template v<c>(i);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) o[b][i] = mfma16(va, as_bf16x8(p[b][c]), o[b][i]);
-    }
+  bf16x8 buf[PD];
+  auto read = [&](auto oc) {
+    constexpr int op = decltype(oc)::value;
+    constexpr int c = op / DB, i = op % DB;
+    if constexpr (i == 0) src.template step<8 + c>();
+    buf[op % PD] = src.template v<c>(i);
   };
-  chunk(std::integral_constant<int, 0>{});
-  chunk(std::integral_constant<int, 1>{});
-  chunk(std::integral_constant<int, 2>{});
-  chunk(std::integral_constant<int, 3>{});
-  chunk(std::integral_constant<int, 4>{});
-  chunk(std::integral_constant<int, 5>{});
-  chunk(std::integral_constant<int, 6>{});
-  chunk(std::integral_constant<int, 7>{});
+  static_for<0, PD>(read);
+  static_for<0, NOP>([&](auto oc) {
+    constexpr int op = decltype(oc)::value;
+    constexpr int c = op / DB, i = op % DB;
+    const bf16x8 va = buf[op % PD];
+    if constexpr (op + PD < NOP) read(std::integral_constant<int, op + PD>{});
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b][i] = mfma16(va, as_bf16x8(p[b][c]), o[b][i]);
+  });
 }
 
 // Q^T operand for d-step t: dims 32t + 8q .. +7 of this lane's query row.
@@ -445,7 +509,9 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
   bf16x8 qf[1][KV<D>::DS];
   load_q<D>(q + ((int64_t)b * nq + hq) * D, live, qf[0]);
   const int pcol[1] = {L - 1};
-  RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1};
+  ChunkLaneOffs<D> offs;
+  offs.init();
+  RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1, &offs};
   src.sp.load(bt + (int64_t)b * max_pages, key0, L - 1);
   src.prologue();
   u32x4 p[1][8];
@@ -509,14 +575,43 @@ constexpr int kPrefillNB = 1;
 // Copy the K or V rows of a whole 256-key split into LDS: thread t's load n
 // fills the 1 KiB block n*4 + t/64 (one page is 16 keys = 4 KiB at d=128,
 // 2 KiB at d=64, so every load stays within one page).
+// Per-lane offsets of a wave's staging loads: load n of wave w covers keys
+// (4n + w)*KPI.., so kfirst mod 32 takes at most two values (by (4n*KPI/16)
+// mod 2).
+template <int D>
+struct StageLaneOffs {
+  uint32_t k[2], v[2];
+  __device__ __forceinline__ void init(int wave) {
+    constexpr int KPI = kWave / KV<D>::CPR;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      k[h] = dma_lane_off<D, true>(16 * h + wave * KPI);
+      v[h] = dma_lane_off<D, false>(16 * h + wave * KPI);
+    }
+  }
+};
+
 template <int D, bool IS_K>
 __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPages& sp, int nkv,
-                                            int g, int key0, int last, uint8_t* lds) {
+                                            int g, int key0, int last, uint8_t* lds,
+                                            const StageLaneOffs<D>& offs) {
   constexpr int KPI = kWave / KV<D>::CPR;       // keys per 1 KiB load
   constexpr int NLOAD = 256 / KPI / 4;          // loads per thread (4 waves)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool hi = ((wave * KPI) >> 4) != 0;     // the wave's keys start in the next page
   const uint32_t base = (uint32_t)(uintptr_t)lds;
+  if (key0 + kSplit - 1 <= last) {
+    const int64_t head = (int64_t)g * 16 * D, stride = (int64_t)nkv * 16 * D;
+#pragma unroll
+    for (int n = 0; n < NLOAD; ++n) {
+      const int pidx = (n * 4 * KPI) >> 4;
+      const int page = (hi && pidx + 1 < 16) ? sp.pg[pidx + 1] : sp.pg[pidx];
+      const int h = ((n * 4 * KPI) >> 4) & 1;
+      lds_dma16_sv(pool + head + page * stride, IS_K ? offs.k[h] : offs.v[h],
+                   base + (uint32_t)((n * 4 + wave) * KPI) * KV<D>::ROWB);
+    }
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < NLOAD; ++n) {
     const int pidx = (n * 4 * KPI) >> 4;        // compile-time after unrolling
@@ -581,12 +676,14 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   }
   SplitPages pages;
   pages.load(bt_row, 0, L - 1);
-  stage_split<D, true>(kc, pages, nkv, g, 0, L - 1, klds);
+  StageLaneOffs<D> soffs;
+  soffs.init(wave);
+  stage_split<D, true>(kc, pages, nkv, g, 0, L - 1, klds, soffs);
   for (int s = 0; s < nsplit; ++s) {
     const int key0 = s * kSplit;
     wait_vmcnt_le<0>();
     __syncthreads();  // K(s) in LDS; every wave is done reading V(s-1)
-    stage_split<D, false>(vc, pages, nkv, g, key0, L - 1, vlds);
+    stage_split<D, false>(vc, pages, nkv, g, key0, L - 1, vlds, soffs);
     SplitPages next;  // the next split's pages, fetched while this one computes
     if (s + 1 < nsplit) next.load(bt_row, key0 + kSplit, L - 1);
     u32x4 p[NB][8];
@@ -596,7 +693,7 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     __syncthreads();  // V(s) in LDS; every wave is done reading K(s)
     if (s + 1 < nsplit) {
       pages = next;
-      stage_split<D, true>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds);
+      stage_split<D, true>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs);
     }
     f32x4 os[NB][DB];
     split_pv<D, NB>(src, p, os);
@@ -666,8 +763,10 @@ __global__ __launch_bounds__(256) void bix_attn_decode_splitkv_kernel(
   const int pcol[1] = {L - 1};
   float M = -INFINITY, Lsum = 0.0f;
   f32x4 O[DB];
+  ChunkLaneOffs<D> offs;
+  offs.init();
   for (int key0 = k_begin; key0 < k_end; key0 += kSplit) {
-    RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1};
+    RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1, &offs};
     src.sp.load(bt + (int64_t)b * max_pages, key0, L - 1);
     src.prologue();
     u32x4 p[1][8];
