@@ -480,46 +480,254 @@ __global__ __launch_bounds__(128) void kv_append_kernel(const uint16_t* __restri
 }
 
 // ---- decode ------------------------------------------------------------------
-// One wave per (sequence b, kv head g, split s); 4 waves per workgroup.
+// Persistent: about one workgroup per CU, 4 waves.  Wave w of NW processes the
+// units u = w, w + NW, w + 2NW, ... of the dense enumeration (kv head g
+// fastest, then sequence b, then split s), skipping splits that start at or
+// past the sequence's length.  Each wave streams its units' chunks through a
+// private ring of 4 slots without a break: while a unit's last chunks are
+// computed, the next unit's first chunks are already loading; the next unit's
+// block-table pages are read, and its q is copied into LDS, one unit ahead.
 // Workspace record per (b, q head, s): o[D], m, l  (fp32).
+constexpr int kDecodeRing = 4;  // divides the 16 chunk loads of a split
+constexpr int kMapSeqs = 256;   // batches up to this size get the balanced unit list
+
+template <int D>
+struct DecodeUnit {
+  SplitPages sp;
+  int g, b, s, key0, last;
+};
+
+template <int D>
+struct StreamSrc {
+  static constexpr int RING = kDecodeRing;
+  static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
+  static constexpr int LOADS = SLOT / 1024;          // 1 KiB loads per chunk
+  static constexpr int AHEAD = RING - 1;             // chunks in flight
+  static constexpr int QLOADS = 16 * KV<D>::ROWB / 1024;  // q copy of the next unit
+  static_assert(16 % RING == 0, "slots repeat every split");
+  static_assert(LOADS * (AHEAD - 1) + QLOADS <= 63, "vmcnt range");
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const uint8_t* ring;
+  const ChunkLaneOffs<D>* offs;
+  int nkv;
+  DecodeUnit<D> cur, nxt;
+  bool has_next;
+
+  // stream position G: chunk G of the current unit (G < 16) or chunk G-16 of
+  // the next one; K chunks are 0..7, V chunks 8..15
+  template <int G>
+  __device__ __forceinline__ void issue() const {
+    constexpr int C = G % 16, CC = C & 7;
+    constexpr bool IS_K = C < 8;
+    constexpr int KPI = kWave / KV<D>::CPR;
+    const DecodeUnit<D>& un = G < 16 ? cur : nxt;
+    const uint32_t dst = (uint32_t)(uintptr_t)(ring + (G % RING) * SLOT);
+    const uint16_t* pool = IS_K ? kc : vc;
+    if (un.key0 + kSplit - 1 <= un.last) {
+      const int64_t head = (int64_t)un.g * 16 * D, stride = (int64_t)nkv * 16 * D;
+#pragma unroll
+      for (int n = 0; n < LOADS; ++n)
+        lds_dma16_sv(pool + head + un.sp.pg[(32 * CC + n * KPI) >> 4] * stride,
+                     IS_K ? offs->k[n] : offs->v[n], dst + (uint32_t)n * 1024);
+      return;
+    }
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n)
+      dma_block<D, IS_K>(pool, un.sp.pg[(32 * CC + n * KPI) >> 4], nkv, un.g, un.key0,
+                         32 * CC + n * KPI, un.last, dst + (uint32_t)n * 1024);
+  }
+  template <int G>
+  __device__ __forceinline__ void prologue_from() const {
+    if constexpr (G < AHEAD) {
+      issue<G>();
+      prologue_from<G + 1>();
+    }
+  }
+  __device__ __forceinline__ void prologue() const { prologue_from<0>(); }
+  // Before chunk IDX of the current unit is read: wait for it (the loads
+  // issued after it are the next AHEAD-1 stream chunks, plus the next unit's
+  // q copy while IDX < AHEAD), then refill the slot of chunk IDX-1.
+  template <int IDX>
+  __device__ __forceinline__ void step() const {
+    if (has_next) {
+      if constexpr (IDX < AHEAD) wait_vmcnt_le<LOADS * (AHEAD - 1) + QLOADS>();
+      else wait_vmcnt_le<LOADS * (AHEAD - 1)>();
+      lds_reads_done();
+      issue<IDX + AHEAD>();
+    } else {
+      wait_vmcnt_le<LOADS * (15 - IDX < AHEAD - 1 ? 15 - IDX : AHEAD - 1)>();
+      if constexpr (IDX + AHEAD < 16) {
+        lds_reads_done();
+        issue<IDX + AHEAD>();
+      }
+    }
+  }
+  template <int C>
+  __device__ __forceinline__ u32x4 k(int h, int t) const {
+    return lds_k_operand<D>(ring + (C % RING) * SLOT, h, t);
+  }
+  template <int C>
+  __device__ __forceinline__ bf16x8 v(int i) const {
+    return lds_v_operand<D>(ring + ((8 + C) % RING) * SLOT, i);
+  }
+};
+
+// The q of a unit (16 columns = the group's heads, padded with copies of a
+// live column, x D) in LDS: column rows of D*2 bytes with their 16-byte chunks
+// XOR-swizzled by column so that the 16 columns a read covers fall on distinct
+// banks.
+template <int D>
+__device__ __forceinline__ int qswz(int col) {
+  if constexpr (D == 128) return col & 15;
+  else return (col >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ void copy_q(const uint16_t* q, int b, int g, int nq, int group,
+                                       uint32_t slot) {
+  constexpr int CPR = KV<D>::CPR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint16_t* base = q + ((int64_t)b * nq + (int64_t)g * group) * D;
+#pragma unroll
+  for (int n = 0; n < 16 * CPR / kWave; ++n) {
+    const int idx = n * kWave + lane, col = idx / CPR, phys = idx % CPR;
+    const int logical = phys ^ qswz<D>(col);
+    const int src_col = min(col, group - 1);
+    lds_dma16_sv(base, (uint32_t)((src_col * D + logical * 8) * 2), slot + (uint32_t)n * 1024);
+  }
+}
+template <int D>
+__device__ __forceinline__ void read_q(const uint8_t* slot, bf16x8 (&qf)[KV<D>::DS]) {
+  const int lane = threadIdx.x & (kWave - 1), col = lane & 15, q4 = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < KV<D>::DS; ++t)
+    qf[t] = as_bf16x8(*(const u32x4*)(slot + col * KV<D>::ROWB + (((4 * t + q4) ^ qswz<D>(col)) << 4)));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
     int smax, float c2) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4][kRing * RingSrc<D>::SLOT];
+  using Src = StreamSrc<D>;
+  constexpr int QSLOT = 16 * KV<D>::ROWB;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[4][Src::RING * Src::SLOT + 2 * QSLOT];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // kv head fastest, then sequence, then split: the waves of a workgroup are
-  // kv heads of one (sequence, split), so they have work or none together
-  const int64_t u = (int64_t)blockIdx.x * 4 + wave;
-  const int g = (int)(u % nkv);
-  const int64_t rest = u / nkv;
-  const int b = (int)(rest % B);
-  const int s = (int)(rest / B);
-  if (s >= smax) return;
-  const int L = kv_len[b];
-  const int key0 = s * kSplit;
-  if (key0 >= L) return;
+  const int64_t NW = (int64_t)gridDim.x * 4;
+  const int64_t total = (int64_t)B * nkv * smax;
   const int group = nq / nkv;
-  const int col = lane & 15;
-  const bool live = col < group;
-  const int hq = g * group + (live ? col : 0);
-  bf16x8 qf[1][KV<D>::DS];
-  load_q<D>(q + ((int64_t)b * nq + hq) * D, live, qf[0]);
-  const int pcol[1] = {L - 1};
+  const uint8_t* ring = lds[wave];
+  const uint32_t qslot0 = (uint32_t)(uintptr_t)(ring + Src::RING * Src::SLOT);
+
+  // Units are dealt round-robin from the list of existing ones only, so every
+  // wave gets the same number (+-1).  The list is sequence-major; sequence b
+  // has nkv * ceil(L_b/256) units, kv head fastest.  For up to kMapSeqs
+  // sequences, a per-lane prefix of those counts (64 sequences per register)
+  // is built once and unit v is located by ballot; larger batches use the
+  // dense (g, b, s) enumeration and skip splits past a sequence's end.
+  constexpr int NCH = kMapSeqs / 64;
+  int incl[NCH];  // inclusive prefix of per-sequence split counts, lane = sequence mod 64
+  int64_t listed = 0;
+  const bool mapped = B <= kMapSeqs;
+  if (mapped) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int bi = c * 64 + lane;
+      const int ns = bi < B ? (kv_len[bi] + kSplit - 1) / kSplit : 0;
+      int x = ns;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+      }
+      incl[c] = x + (int)(listed / nkv);
+      listed += (int64_t)__builtin_amdgcn_readlane(x, 63) * nkv;
+    }
+  }
+  const int64_t total_units = mapped ? listed : total;
+  // the first unit at or after u that exists (total_units if none)
+  auto next_valid = [&](int64_t u) {
+    if (mapped) return u < total_units ? u : total_units;
+    for (; u < total; u += NW) {
+      const int b = (int)((u / nkv) % B), s = (int)(u / nkv / B);
+      if (s * kSplit < kv_len[b]) break;
+    }
+    return u;
+  };
+  auto fill = [&](DecodeUnit<D>& un, int64_t u) {
+    if (mapped) {
+      const int64_t sp = u / nkv;  // split index in the sequence-major list
+      int b = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        // sequences of this register whose splits all come before sp
+        b += __builtin_popcountll(__ballot((int64_t)incl[c] <= sp));
+      }
+      // splits of the sequences before b: the inclusive prefix of sequence b-1
+      int before = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        if (b >= 1 && (b - 1) / 64 == c) before = __builtin_amdgcn_readlane(incl[c], (b - 1) % 64);
+      un.b = b;
+      un.s = (int)(sp - before);
+      un.g = (int)(u % nkv);
+    } else {
+      un.g = (int)(u % nkv);
+      un.b = (int)((u / nkv) % B);
+      un.s = (int)(u / nkv / B);
+    }
+    // every field is wave-uniform; say so, so that they live in scalar registers
+    un.g = __builtin_amdgcn_readfirstlane(un.g);
+    un.b = __builtin_amdgcn_readfirstlane(un.b);
+    un.s = __builtin_amdgcn_readfirstlane(un.s);
+    un.key0 = un.s * kSplit;
+    un.last = __builtin_amdgcn_readfirstlane(kv_len[un.b] - 1);
+    un.sp.load(bt + (int64_t)un.b * max_pages, un.key0, un.last);
+  };
+
+  int64_t u = next_valid((int64_t)blockIdx.x * 4 + wave);
+  if (u >= total_units) return;
   ChunkLaneOffs<D> offs;
   offs.init();
-  RingSrc<D> src{kc, vc, ring[wave], {}, nkv, g, key0, L - 1, &offs};
-  src.sp.load(bt + (int64_t)b * max_pages, key0, L - 1);
+  Src src{kc, vc, ring, &offs, nkv, {}, {}, false};
+  fill(src.cur, u);
+  int qi = 0;
+  copy_q<D>(q, src.cur.b, src.cur.g, nq, group, qslot0);
   src.prologue();
-  u32x4 p[1][8];
-  float m[1], l[1];
-  f32x4 o[1][KV<D>::DB];
-  split_qk<D, 1>(src, key0, INT_MAX, L - 1, qf, pcol, c2, p, m, l);
-  split_pv<D, 1>(src, p, o);
-  if (live) store_partial<D>(ws + (((int64_t)b * nq + hq) * smax + s) * (D + 2), o[0], m[0], l[0]);
+  const int col = lane & 15;
+  const bool live = col < group;
+  while (true) {
+    const int64_t un = next_valid(u + NW);
+    src.has_next = un < total_units;
+    if (src.has_next) {
+      fill(src.nxt, un);
+      copy_q<D>(q, src.nxt.b, src.nxt.g, nq, group, qslot0 + (uint32_t)(qi ^ 1) * QSLOT);
+    }
+    // this unit's q copy is older than every chunk of the unit and than the
+    // next unit's q copy
+    wait_vmcnt_le<Src::LOADS * Src::AHEAD + Src::QLOADS>();
+    bf16x8 qf[1][KV<D>::DS];
+    read_q<D>(ring + Src::RING * Src::SLOT + qi * QSLOT, qf[0]);
+    const int L = src.cur.last + 1;
+    const int pcol[1] = {L - 1};
+    u32x4 p[1][8];
+    float m[1], l[1];
+    f32x4 o[1][KV<D>::DB];
+    split_qk<D, 1>(src, src.cur.key0, INT_MAX, L - 1, qf, pcol, c2, p, m, l);
+    split_pv<D, 1>(src, p, o);
+    if (live) {
+      const int hq = src.cur.g * group + col;
+      store_partial<D>(ws + (((int64_t)src.cur.b * nq + hq) * smax + src.cur.s) * (D + 2), o[0],
+                       m[0], l[0]);
+    }
+    if (!src.has_next) break;
+    u = un;
+    src.cur = src.nxt;
+    qi ^= 1;
+  }
+  wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
 }
 
 // Fold the splits of one (sequence, q head) left in ascending order.
@@ -830,11 +1038,27 @@ hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* 
   return hipGetLastError();
 }
 
+// Workgroups of the persistent decode kernel: one per CU (each uses all of
+// a CU's LDS), fewer when there are fewer units.
+static int decode_workgroups(int64_t units) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  const int64_t need = (units + 3) / 4;
+  return (int)(need < cus ? need : cus);
+}
+
 hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
                               const int32_t* bt, const void* kc, const void* vc, void* out,
                               float* lse, int max_splits, float* ws, hipStream_t st) {
   const int64_t units = (int64_t)s.B * s.nkv * max_splits;
-  const dim3 grid1((unsigned)((units + 3) / 4)), grid2((unsigned)((int64_t)s.B * s.nq));
+  const dim3 grid1((unsigned)decode_workgroups(units)), grid2((unsigned)((int64_t)s.B * s.nq));
   const float c2 = base2_scale(s.scale);
   if (s.d == 128) {
     hipLaunchKernelGGL(bi_attn_decode_partial_kernel<128>, grid1, dim3(256), 0, st,
