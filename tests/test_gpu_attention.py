@@ -175,3 +175,28 @@ def test_repeat_bitwise():
             base = cur
         for a, b in zip(base, cur):
             assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("B,maxlen", [(300, 600), (256, 2048)])
+def test_decode_large_and_mixed_batches(orc, B, maxlen):
+    """Decode over batches at and past the size the balanced unit list
+    covers (256 sequences), with sequences from 1 to 8 splits: every decoded
+    row equals the same row of a one-shot prefill.  8 q heads over 2 kv heads
+    (group 4, d=128) keep the inputs small; the unit list does not depend on
+    the head counts."""
+    rng = synth.stream(31, "large_batch.lens")
+    lens = [int(x) for x in rng.integers(2, maxlen + 1, size=B)]
+    lens[0], lens[-1] = 2, maxlen  # shortest and longest in one batch
+    prob = synth.attn_problem(lens, n_q=8, n_kv=2, d=128, seed=31,
+                              tags=["lb%d" % i for i in range(B)])
+    one = PagedRun(prob, page_seed=1)
+    one.prefill([(b, L) for b, L in enumerate(lens)])
+    dec = PagedRun(prob, page_seed=2)
+    dec.prefill([(b, L - 2) for b, L in enumerate(lens)])
+    dec.decode(list(range(B)))
+    dec.decode(list(range(B)))
+    for b, L in enumerate(lens):
+        assert np.array_equal(dec.out[b][L - 2:], one.out[b][L - 2:]), b
+        assert np.array_equal(dec.lse[b][L - 2:].view(np.uint32), one.lse[b][L - 2:].view(np.uint32)), b
+    picks = [(b, lens[b] - 1) for b in (0, 1, B // 2, B - 1)]
+    _parity(orc, prob, dec, picks)
