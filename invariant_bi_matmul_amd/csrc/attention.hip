@@ -74,6 +74,15 @@ struct KV {
   using vrow = std::conditional_t<D == 128, u32x4, u32x2>;  // DB dims of one key
 };
 
+// Calls f(integral_constant<int, i>) for i = I .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // In-chunk key of the S^T A-operand row this lane loads for half h.
 __device__ __forceinline__ int okey_k(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -130,14 +139,27 @@ __device__ __forceinline__ bf16x8 lds_v_operand(const uint8_t* rows, int i) {
 // wave-uniform (scalar registers).
 struct SplitPages {
   int pg[16];
-  int pg_last;
   __device__ __forceinline__ void load(const int32_t* bt_row, int key0, int last) {
+    if (key0 + 255 <= last) {
+      // a fully written split: 16 consecutive block-table entries
+      const int32_t* row = bt_row + (key0 >> 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      pg[i] = __builtin_amdgcn_readfirstlane(bt_row[min(key0 + 16 * i, last) >> 4]);
-    pg_last = __builtin_amdgcn_readfirstlane(bt_row[last >> 4]);
+      for (int i = 0; i < 16; ++i) pg[i] = __builtin_amdgcn_readfirstlane(row[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pg[i] = __builtin_amdgcn_readfirstlane(bt_row[min(key0 + 16 * i, last) >> 4]);
+    }
   }
 };
+
+// Start of the (page, kv head) block of a pool whose kv-head-g base is
+// pool_g: pages are page_elems = nkv*16*D elements apart (a 32 x 32 -> 64-bit
+// product of bytes).
+__device__ __forceinline__ const uint16_t* page_block(const uint16_t* pool_g, int page,
+                                                      uint32_t page_elems) {
+  return (const uint16_t*)((const uint8_t*)pool_g + (uint64_t)(uint32_t)page * (2u * page_elems));
+}
 
 // Byte offset, inside one (page, kv head) block, of the 16-byte chunk a lane
 // of a direct load fetches for split key kl = kfirst + lane/CPR when no
@@ -229,12 +251,15 @@ struct RingSrc {
     constexpr int KPI = kWave / KV<D>::CPR;
     const uint32_t dst = (uint32_t)(uintptr_t)(ring + (IDX % RING) * SLOT);
     if (key0 + kSplit - 1 <= last) {
-      const int64_t head = (int64_t)g * 16 * D, stride = (int64_t)nkv * 16 * D;
-      const uint16_t* pool = IDX < 8 ? kc : vc;
-#pragma unroll
-      for (int n = 0; n < LOADS; ++n)
-        lds_dma16_sv(pool + head + sp.pg[(32 * C + n * KPI) >> 4] * stride,
-                     IDX < 8 ? offs->k[n] : offs->v[n], dst + (uint32_t)n * 1024);
+      const uint16_t* pool_g = (IDX < 8 ? kc : vc) + (int64_t)g * 16 * D;
+      const uint32_t page_elems = (uint32_t)nkv * 16 * D;
+      const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+      static_for<0, LOADS>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        lds_dma16_si<(IDX % RING) * SLOT + n * 1024>(
+            page_block(pool_g, sp.pg[(32 * C + n * KPI) >> 4], page_elems),
+            IDX < 8 ? offs->k[n] : offs->v[n], ring0);
+      });
       return;
     }
 #pragma unroll
@@ -281,14 +306,6 @@ struct RingSrc {
 // invalid), and leaves in p[b][c] the bf16 weights of keys key0+32c+8q+0..7.
 // pmin (wave-uniform) is at most the position of every column whose result is
 // used: a chunk whose last key is <= pmin and < key_end needs no masking.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // LDS operand reads are issued this many MFMA operands ahead of their use, so
 // their latency hides behind the MFMAs in between (one wave per SIMD: nothing
 // else would hide it).
@@ -525,11 +542,15 @@ struct StreamSrc {
     const uint32_t dst = (uint32_t)(uintptr_t)(ring + (G % RING) * SLOT);
     const uint16_t* pool = IS_K ? kc : vc;
     if (un.key0 + kSplit - 1 <= un.last) {
-      const int64_t head = (int64_t)un.g * 16 * D, stride = (int64_t)nkv * 16 * D;
-#pragma unroll
-      for (int n = 0; n < LOADS; ++n)
-        lds_dma16_sv(pool + head + un.sp.pg[(32 * CC + n * KPI) >> 4] * stride,
-                     IS_K ? offs->k[n] : offs->v[n], dst + (uint32_t)n * 1024);
+      const uint16_t* pool_g = pool + (int64_t)un.g * 16 * D;
+      const uint32_t page_elems = (uint32_t)nkv * 16 * D;
+      const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+      static_for<0, LOADS>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        lds_dma16_si<(G % RING) * SLOT + n * 1024>(
+            page_block(pool_g, un.sp.pg[(32 * CC + n * KPI) >> 4], page_elems),
+            IS_K ? offs->k[n] : offs->v[n], ring0);
+      });
       return;
     }
 #pragma unroll
@@ -809,15 +830,17 @@ __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPag
   const bool hi = ((wave * KPI) >> 4) != 0;     // the wave's keys start in the next page
   const uint32_t base = (uint32_t)(uintptr_t)lds;
   if (key0 + kSplit - 1 <= last) {
-    const int64_t head = (int64_t)g * 16 * D, stride = (int64_t)nkv * 16 * D;
-#pragma unroll
-    for (int n = 0; n < NLOAD; ++n) {
-      const int pidx = (n * 4 * KPI) >> 4;
+    const uint16_t* pool_g = pool + (int64_t)g * 16 * D;
+    const uint32_t page_elems = (uint32_t)nkv * 16 * D;
+    const uint32_t wbase = base + (uint32_t)(wave * KPI * KV<D>::ROWB);
+    static_for<0, NLOAD>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      constexpr int pidx = (n * 4 * KPI) >> 4;
       const int page = (hi && pidx + 1 < 16) ? sp.pg[pidx + 1] : sp.pg[pidx];
-      const int h = ((n * 4 * KPI) >> 4) & 1;
-      lds_dma16_sv(pool + head + page * stride, IS_K ? offs.k[h] : offs.v[h],
-                   base + (uint32_t)((n * 4 + wave) * KPI) * KV<D>::ROWB);
-    }
+      constexpr int h = ((n * 4 * KPI) >> 4) & 1;
+      lds_dma16_si<n * 4 * KPI * KV<D>::ROWB>(page_block(pool_g, page, page_elems),
+                                              IS_K ? offs.k[h] : offs.v[h], wbase);
+    });
     return;
   }
 #pragma unroll

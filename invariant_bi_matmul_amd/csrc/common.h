@@ -95,6 +95,20 @@ __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, u
                : "s"(m0v), "v"(voff), "s"(ub)
                : "memory", "m0");
 }
+// The same load to LDS address m0base + IMM (m0base wave-uniform): M0 is
+// formed by one scalar add inside the asm.
+template <int IMM>
+__device__ __forceinline__ void lds_dma16_si(const void* sbase, uint32_t voff, uint32_t m0base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(m0base);
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t ub =
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+      (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m), "v"(voff), "s"(ub), "n"(IMM)
+               : "memory", "m0", "scc");
+}
 #pragma clang diagnostic pop
 // Make the compiler wait for a value's load here (an empty asm that reads
 // it), before any untracked load is issued after it.
