@@ -51,7 +51,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // One step of the left fold:  m' = max(m, ms); l = l e^(m-m') + ls e^(ms-m'),
-// o = o e^(m-m') + os e^(ms-m') (base-2 logits, so e^ is exp2).
+// o = o e^(m-m') + os e^(ms-m') (base-2 logits, so e^ is exp2; the first
+// product is fused into the add).
 struct FoldCoef {
   float a, b, m;
 };
@@ -60,7 +61,7 @@ __device__ __forceinline__ FoldCoef fold_coef(float m, float ms) {
   return FoldCoef{fast_exp2(m - mn), fast_exp2(ms - mn), mn};
 }
 __device__ __forceinline__ float fold_apply(float x, float xs, const FoldCoef& f) {
-  return x * f.a + xs * f.b;
+  return fmaf(x, f.a, xs * f.b);
 }
 // Natural-log lse from base-2 max and sum.
 __device__ __forceinline__ float lse_of(float m2, float l) { return (m2 + fast_log2(l)) * kLn2; }
@@ -193,21 +194,52 @@ __device__ __forceinline__ void dma_block(const uint16_t* pool, int page, int nk
   lds_dma16_sv(base, (uint32_t)(slot * D + logical * 8) * 2, lds_block);
 }
 
+// LDS addresses of this lane's operand reads in chunk 0 of a K / V region
+// (the same addressing as lds_k_operand / lds_v_operand), so that a read of
+// chunk C is one LDS load with an immediate offset.
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+template <int D>
+struct OperandLanes {
+  uint32_t k[2][KV<D>::DS];  // (half h, d-step t)
+  uint32_t v[KV<D>::DB][2];  // (dim block i, key half hh)
+  __device__ __forceinline__ void init(uint32_t kregion, uint32_t vregion) {
+    const int lane = threadIdx.x & (kWave - 1), r = lane & 15, q = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < KV<D>::DS; ++t) {
+        const int kk = okey_k(h, r);
+        k[h][t] = kregion + kk * KV<D>::ROWB + (((4 * t + q) ^ kswz<D>(kk)) << 4);
+      }
+#pragma unroll
+    for (int i = 0; i < KV<D>::DB; ++i)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int d = 16 * i + 4 * (r & 3), kk = 8 * q + 4 * hh + (r >> 2);
+        v[i][hh] = vregion + kk * KV<D>::ROWB + (((d >> 3) ^ vswz<D>(kk)) << 4) + (d & 7) * 2;
+      }
+  }
+};
+
 // A whole split staged in LDS by the workgroup (prefill): K and V rows of
-// keys 0..255 at kbase / vbase.
+// keys 0..255 at the regions OperandLanes was built for.
 template <int D>
 struct StagedSrc {
-  const uint8_t* kbase;
-  const uint8_t* vbase;
+  OperandLanes<D> ol;
   template <int IDX>
   __device__ __forceinline__ void step() const {}
   template <int C>
   __device__ __forceinline__ u32x4 k(int h, int t) const {
-    return lds_k_operand<D>(kbase + 32 * C * KV<D>::ROWB, h, t);
+    return *(lds_u32x4*)(uintptr_t)(ol.k[h][t] + 32 * C * KV<D>::ROWB);
   }
   template <int C>
   __device__ __forceinline__ bf16x8 v(int i) const {
-    return lds_v_operand<D>(vbase + 32 * C * KV<D>::ROWB, i);
+    s16x4 x[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      x[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(uintptr_t)(ol.v[i][hh] + 32 * C * KV<D>::ROWB));
+    return join_tr(x[0], x[1]);
   }
 };
 
@@ -894,7 +926,8 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   const int pmin = start + tile * per_wg + wave * NB * ppb;
   const int nsplit = pmax / kSplit + 1;
   const int32_t* bt_row = bt + (int64_t)b * max_pages;
-  const StagedSrc<D> src{klds, vlds};
+  StagedSrc<D> src;
+  src.ol.init((uint32_t)(uintptr_t)klds, (uint32_t)(uintptr_t)vlds);
 
   float M[NB], Lsum[NB];
   f32x4 O[NB][DB];
