@@ -72,31 +72,58 @@ __device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
 // c ^ swz_w(k) (64-byte block XOR).
 __device__ __forceinline__ int swz_w(int k) { return (k & 3) << 2; }
 
+// Position of raster id `id` (groups of GROUP_M row-tiles; row-tiles fastest
+// inside a group, then columns).
+__device__ __forceinline__ void raster_tile(uint32_t id, int tiles_m, int tiles_n, int& m0,
+                                            int& n0) {
+  const uint32_t per_group = (uint32_t)Tile::GROUP_M * (uint32_t)tiles_n;
+  const int grp = (int)(id / per_group);
+  const int grp_rows = min(Tile::GROUP_M, tiles_m - grp * Tile::GROUP_M);
+  const uint32_t within = id - (uint32_t)grp * per_group;
+  m0 = (grp * Tile::GROUP_M + (int)(within % (uint32_t)grp_rows)) * Tile::BM;
+  n0 = (int)(within / (uint32_t)grp_rows) * Tile::BN;
+}
+
+// Persistent: the invariant launch has about one workgroup per CU.  Workgroup
+// b belongs to group x = b mod X (X = min(8, grid); with a grid that is a
+// multiple of 8 the groups are the XCDs, which receive workgroups round-robin)
+// and the groups own contiguous ranges of the raster order, so a group's
+// resident tiles share a block of A and W in its L2.  A workgroup runs its
+// tiles back to back through one continuous stream of k-tiles: the ring
+// loads the next tile's first k-tiles while the current tile finishes.  The
+// split-K comparator launches one workgroup per (tile, slice) instead.
 template <bool SPLIT>
 __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ W,
                                                              void* __restrict__ C, int M, int N,
                                                              int K, int out_f32, int kt_per_split) {
   using T = Tile;
-  constexpr int BM = T::BM, BN = T::BN, BK = T::BK, NT = T::NT, KS = T::KS, STAGES = T::STAGES;
+  constexpr int BK = T::BK, NT = T::NT, KS = T::KS, STAGES = T::STAGES;
   constexpr int MI = T::MI, NI = T::NI, STAGE = T::STAGE, A_BYTES = T::A_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  const uint32_t id = xcd_contiguous_id(blockIdx.x, (uint32_t)(tiles_m * tiles_n));
-  const uint32_t per_group = (uint32_t)T::GROUP_M * (uint32_t)tiles_n;
-  const int grp = (int)(id / per_group);
-  const int grp_rows = min(T::GROUP_M, tiles_m - grp * T::GROUP_M);
-  const uint32_t within = id - (uint32_t)grp * per_group;
-  const int tm = grp * T::GROUP_M + (int)(within % (uint32_t)grp_rows);
-  const int tn = (int)(within / (uint32_t)grp_rows);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int tiles_m = (M + T::BM - 1) / T::BM;
+  const int tiles_n = (N + T::BN - 1) / T::BN;
+  const uint32_t ntiles = (uint32_t)tiles_m * (uint32_t)tiles_n;
 
+  // this workgroup's tiles: first, first + step, ... (count of them)
+  uint32_t first, step, count;
   int kt0 = 0, kt1 = K / BK;
   if (SPLIT) {
+    first = xcd_contiguous_id(blockIdx.x, ntiles);
+    step = 1;
+    count = 1;
     kt0 = (int)blockIdx.z * kt_per_split;
     kt1 = min(kt1, kt0 + kt_per_split);
+  } else {
+    const uint32_t G = gridDim.x, X = G < 8 ? G : 8;
+    const uint32_t x = blockIdx.x % X, j = blockIdx.x / X;
+    const uint32_t gx = G / X + (x < G % X ? 1 : 0);  // workgroups in group x
+    const uint32_t q = ntiles / X, r = ntiles % X;
+    const uint32_t lo = x * q + (x < r ? x : r), hi = lo + q + (x < r ? 1 : 0);
+    first = lo + j;
+    step = gx;
+    count = first < hi ? (hi - first + step - 1) / step : 0;
   }
   const int nk = kt1 - kt0;
 
@@ -105,28 +132,92 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wave_m = wave / T::WAVES_N, wave_n = wave % T::WAVES_N;
 
+  // Epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4.
+  auto store_tile = [&](int m0, int n0, const f32x16 (&acc)[MI][NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = n0 + wave_n * T::WN + ni * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wave_m * T::WM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < M && col < N) {
+            const int64_t o = (int64_t)row * N + col;
+            const float v = acc[mi][ni][r];
+            if (SPLIT) {
+              ((float*)C)[(int64_t)blockIdx.z * M * N + o] = v;
+            } else if (out_f32) {
+              ((float*)C)[o] = v;
+            } else {
+              ((uint16_t*)C)[o] = (uint16_t)f32_to_bf16(v);
+            }
+          }
+        }
+      }
+    }
+  };
+  f32x16 acc[MI][NI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
+  if (nk <= 0) {  // K = 0: every tile is zero
+    for (uint32_t t = 0; t < count; ++t) {
+      int m0, n0;
+      raster_tile(first + t * step, tiles_m, tiles_n, m0, n0);
+      store_tile(m0, n0, acc);
+    }
+    return;
+  }
+
+  // ---- the load side: a cursor over the stream of (tile, k-tile) ----------
   // Direct loads: load i of wave w fills the 1 KiB LDS block i*NT/64 + w of
   // the stage's A (or W) part; lane l of it lands at chunk i*NT + 64w + l.
   // Sources are byte offsets from a wave-uniform per-tile base (rows past M
   // clamp to M-1, columns past N to N-8).
   uint32_t a_off[T::A_LOADS], w_off[T::W_LOADS];
+  const uint8_t* a_base;
+  const uint8_t* w_base;
+  auto load_tile = [&](uint32_t t) __attribute__((always_inline)) {
+    int m0, n0;
+    raster_tile(first + t * step, tiles_m, tiles_n, m0, n0);
 #pragma unroll
-  for (int i = 0; i < T::A_LOADS; ++i) {
-    const int q = i * NT + wave * 64 + lane;
-    const int row = q / T::A_CPR, c = (q % T::A_CPR) ^ swz_a(q / T::A_CPR);
-    a_off[i] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + c * 8) * 2);
-  }
+    for (int i = 0; i < T::A_LOADS; ++i) {
+      const int q = i * NT + wave * 64 + lane;
+      const int row = q / T::A_CPR, c = (q % T::A_CPR) ^ swz_a(q / T::A_CPR);
+      a_off[i] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + c * 8) * 2);
+    }
 #pragma unroll
-  for (int i = 0; i < T::W_LOADS; ++i) {
-    const int q = i * NT + wave * 64 + lane;
-    const int k = q / T::W_CPR, c = (q % T::W_CPR) ^ swz_w(q / T::W_CPR);
-    w_off[i] = (uint32_t)(((int64_t)k * N + min(n0 + c * 8, N - 8) - n0) * 2);
-  }
-  const uint8_t* a_base = (const uint8_t*)(A + (int64_t)m0 * K);
-  const uint8_t* w_base = (const uint8_t*)(W + n0);
+    for (int i = 0; i < T::W_LOADS; ++i) {
+      const int q = i * NT + wave * 64 + lane;
+      const int k = q / T::W_CPR, c = (q % T::W_CPR) ^ swz_w(q / T::W_CPR);
+      w_off[i] = (uint32_t)(((int64_t)k * N + min(n0 + c * 8, N - 8) - n0) * 2);
+    }
+    a_base = (const uint8_t*)(A + (int64_t)m0 * K);
+    w_base = (const uint8_t*)(W + n0);
+  };
+  const int64_t total = (int64_t)count * nk;  // stream length
+  int64_t ipos = 0;                            // stream position of the next load
+  uint32_t it = 0;                             // its tile (index into this workgroup's list)
+  int ikt = 0;                                 // its k-tile within the tile
+  load_tile(0);
+  // The cursor stops at the last position: past the end the last k-tile is
+  // loaded again into a stage nobody reads, so every k-tile issues exactly
+  // one tile of loads and vmcnt counts stay exact.
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (ipos + 1 < total) {
+      ++ipos;
+      if (++ikt == nk) {
+        ikt = 0;
+        load_tile(++it);
+      }
+    }
+  };
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // loads [lo, hi) of k-tile kt (A loads first, then W) into `stage`
-  auto issue = [&](int kt, int stage, int lo, int hi) {
+  // loads [lo, hi) of the cursor's k-tile (A loads first, then W) into `stage`
+  auto issue = [&](int stage, int lo, int hi) __attribute__((always_inline)) {
+    const int kt = kt0 + ikt;
     const uint8_t* ab = a_base + (int64_t)kt * (BK * 2);
     const uint8_t* wb = w_base + (int64_t)kt * BK * N * 2;
     const uint32_t sb = lds0 + stage * STAGE + wave * 1024;
@@ -163,13 +254,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
     wo[ni] = (uint32_t)(A_BYTES + k * T::W_ROW + (((nb >> 3) ^ swz_w(k)) << 4) + (nb & 7) * 2);
   }
 
-  f32x16 acc[MI][NI];
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
-
-  auto frags = [&](const uint8_t* S, int kk, bf16x8 (&af)[MI], bf16x8 (&bw)[NI]) {
+  auto frags = [&](const uint8_t* S, int kk, bf16x8 (&af)[MI], bf16x8 (&bw)[NI]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) af[mi] = as_bf16x8(*(const u32x4*)(S + ao[kk][mi]));
 #pragma unroll
@@ -183,17 +268,20 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
     }
   };
 
-  // One k-tile held in stage S.  Every tile issues exactly one tile of loads
-  // (the index clamps at the end, re-loading the last k-tile into the stage
-  // nobody reads again), so the vector-memory counter says exactly when tile
-  // k has landed: at most STAGES-2 younger tiles may be outstanding.
+  // ---- the compute side ------------------------------------------------
+  uint32_t ct = 0;  // tile being accumulated
+  int ckt = 0;      // its k-tiles done
+  int cm0, cn0;
+  raster_tile(first, tiles_m, tiles_n, cm0, cn0);
+  // One k-tile held in stage S: at most STAGES-2 younger k-tiles may still be
+  // loading when it is needed.
   bf16x8 fa[2][MI], fb[2][NI];
-  auto tile = [&](auto sc, int k) {
+  auto ktile = [&](auto sc) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     const uint8_t* Sp = smem + S * STAGE;
     wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
-    __syncthreads();  // tile k visible; every wave is done with tile k-1's stage
-    const int kn = kt0 + min(k + STAGES - 1, nk - 1), sn = (S + STAGES - 1) % STAGES;
+    __syncthreads();  // k-tile visible; every wave is done with the previous stage
+    constexpr int sn = (S + STAGES - 1) % STAGES;
     frags(Sp, 0, fa[0], fb[0]);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -214,52 +302,40 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KS) {
-        issue(kn, sn, kk * T::LOADS_PER_STEP, min((kk + 1) * T::LOADS_PER_STEP, T::LOADS));
+        issue(sn, kk * T::LOADS_PER_STEP, min((kk + 1) * T::LOADS_PER_STEP, T::LOADS));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    advance();
+    if (++ckt == nk) {  // the tile is complete
+      store_tile(cm0, cn0, acc);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
+      ckt = 0;
+      if (++ct < count) raster_tile(first + ct * step, tiles_m, tiles_n, cm0, cn0);
+    }
   };
-  if (nk > 0) {
+  if (count == 0) return;
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue(kt0 + min(s, nk - 1), s, 0, T::LOADS);
-    static_assert(STAGES == 3, "the loop below is unrolled by the ring depth");
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    int k = 0;
-    for (; k + 3 <= nk; k += 3) {
-      tile(S0{}, k);
-      tile(S1{}, k + 1);
-      tile(S2{}, k + 2);
-    }
-    if (k < nk) tile(S0{}, k);
-    if (k + 1 < nk) tile(S1{}, k + 1);
-    wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
+  for (int s = 0; s < STAGES - 1; ++s) {
+    issue(s, 0, T::LOADS);
+    advance();
   }
-
-  // Epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4.
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int col = n0 + wave_n * T::WN + ni * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wave_m * T::WM + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < M && col < N) {
-          const int64_t o = (int64_t)row * N + col;
-          const float v = acc[mi][ni][r];
-          if (SPLIT) {
-            ((float*)C)[(int64_t)blockIdx.z * M * N + o] = v;
-          } else if (out_f32) {
-            ((float*)C)[o] = v;
-          } else {
-            ((uint16_t*)C)[o] = (uint16_t)f32_to_bf16(v);
-          }
-        }
-      }
-    }
+  static_assert(STAGES == 3, "the loop below is unrolled by the ring depth");
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  int64_t p = 0;
+  for (; p + 3 <= total; p += 3) {
+    ktile(S0{});
+    ktile(S1{});
+    ktile(S2{});
   }
+  if (p < total) ktile(S0{});
+  if (p + 1 < total) ktile(S1{});
+  wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
 }
 
 // Sum split-K partials in slice order, then round.
@@ -279,10 +355,25 @@ __global__ __launch_bounds__(256) void bix_matmul_reduce_kernel(const float* __r
 
 }  // namespace
 
+// Compute units of the current device (one persistent workgroup each).
+static int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
                          int64_t k, hipStream_t st) {
   const int64_t tiles = ((m + Tile::BM - 1) / Tile::BM) * ((n + Tile::BN - 1) / Tile::BN);
-  hipLaunchKernelGGL((bi_matmul_kernel<false>), dim3((unsigned)tiles), dim3(Tile::NT), 0, st,
+  const int64_t grid = tiles < device_cus() ? tiles : device_cus();
+  hipLaunchKernelGGL((bi_matmul_kernel<false>), dim3((unsigned)grid), dim3(Tile::NT), 0, st,
                      (const uint16_t*)a, (const uint16_t*)w, c, (int)m, (int)n, (int)k,
                      c_f32 ? 1 : 0, 0);
   return hipGetLastError();
