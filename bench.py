@@ -248,6 +248,75 @@ def comparators(wl):
     return out
 
 
+def _paged(wl, lens, tag):
+    """A paged pool (seeded page permutation) for `lens`, drawn on the GPU."""
+    import torch
+    np, synth, dev = wl.np, wl.synth, wl.dev
+    pages = [(l + 15) // 16 for l in lens]
+    num = sum(pages) + 3
+    perm = synth.stream(0, tag + ".pages").permutation(num).astype(np.int32)
+    bt = np.full((len(lens), max(pages)), -1, dtype=np.int32)
+    cur = 0
+    for b, p in enumerate(pages):
+        bt[b, :p] = perm[cur:cur + p]
+        cur += p
+    kc = synth.device_normal_bf16((num, NKV, 16, D), 0.0, 1.0, 0, tag + ".k", dev)
+    vc = synth.device_normal_bf16((num, NKV, 16, D), 0.0, 1.0, 0, tag + ".v", dev)
+    return kc, vc, torch.from_numpy(bt).to(dev)
+
+
+def more_sizes(wl):
+    """The same kernels at the other sizes the workload names (RMSNorm over
+    16384 rows at H 4096 and 8192, decode B=16 ragged L<=32768, one-shot
+    prefill of 2 x 4096), and, for context, the vendor GEMM (torch.matmul,
+    not batch-invariant) at the step's matmul shape.  Warm timings."""
+    import torch
+    bi, synth, dev = wl.bi, wl.synth, wl.dev
+    out = {}
+    for h in (4096, 8192):
+        x = synth.device_normal_bf16((16384, h), 0.0, 1.0, 0, "bench.rms16k.x%d" % h, dev)
+        g = synth.device_normal_bf16((h,), 1.0, 0.1, 0, "bench.rms16k.g%d" % h, dev)
+        y = torch.empty_like(x)
+        ms = time_call(lambda: bi.rmsnorm(x, g, wl.eps, out=y))
+        gbs = (2 * 16384 * h * 2 + 2 * h) / ms / 1e6
+        out["rmsnorm_R16384_H%d" % h] = {"ms": ms, "GB/s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        del x, y
+    lens, _ = synth.ragged_lengths(16, 32768, seed=0)
+    kc, vc, bt = _paged(wl, lens, "bench.dec32k")
+    q = synth.device_normal_bf16((16, NQ, D), 0.0, 1.0, 0, "bench.dec32k.q", dev)
+    kn = synth.device_normal_bf16((16, NKV, D), 0.0, 1.0, 0, "bench.dec32k.kn", dev)
+    vn = synth.device_normal_bf16((16, NKV, D), 0.0, 1.0, 0, "bench.dec32k.vn", dev)
+    kvl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = torch.empty(16, NQ, D, dtype=torch.bfloat16, device=dev)
+    ms = time_call(lambda: bi.attn_decode(q, kn, vn, kvl, bt, kc, vc, wl.scale, 32768, out=o))
+    by = sum(lens) * NKV * D * 2 * 2 + 16 * NQ * D * 2 * 2 + 16 * NKV * D * 2 * 2
+    out["decode_B16_L32768"] = {"ms": ms, "GB/s": by / ms / 1e6,
+                                "hbm_frac": by / ms / 1e6 / HBM_PEAK_GBS}
+    del kc, vc
+    L = 4096
+    kc, vc, bt = _paged(wl, [L, L], "bench.pre2x4k")
+    q = synth.device_normal_bf16((2 * L, NQ, D), 0.0, 1.0, 0, "bench.pre2x4k.q", dev)
+    kn = synth.device_normal_bf16((2 * L, NKV, D), 0.0, 1.0, 0, "bench.pre2x4k.kn", dev)
+    vn = synth.device_normal_bf16((2 * L, NKV, D), 0.0, 1.0, 0, "bench.pre2x4k.vn", dev)
+    cu = torch.tensor([0, L, 2 * L], dtype=torch.int32, device=dev)
+    kvl = torch.tensor([L, L], dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    ms = time_call(lambda: bi.attn_prefill(q, kn, vn, cu, kvl, bt, kc, vc, wl.scale, L, out=o),
+                   reps=5)
+    fl = 4.0 * D * NQ * 2 * sum(p + 1 for p in range(L))
+    out["prefill_2x4096_one_shot"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                                      "mfma_frac": fl / ms / 1e9 / MFMA_BF16_PEAK}
+    del kc, vc, q, o
+    cv = torch.empty_like(wl.c)
+    tv = time_call(lambda: torch.matmul(wl.y, wl.w, out=cv))
+    ti = time_call(lambda: bi.matmul(wl.y, wl.w, out=wl.c))
+    out["vendor_gemm_M%d_N%d_K%d" % (M, N, K)] = {
+        "torch_matmul_ms": tv, "torch_matmul_TFLOP/s": 2.0 * M * N * K / tv / 1e9,
+        "invariant_ms": ti, "invariant_over_vendor": ti / tv}
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(wl, target_s=10.0):
     """The fp64 oracle, as it stands, on a bounded sample of the step's matmul:
     rows of A (the RMSNorm output) times the full W, timed on this host."""
@@ -345,6 +414,8 @@ def main():
         log("bench: invariance check and comparators")
         extras["invariance_bitwise"] = invariance_check(wl)
         extras["cost_of_invariance"] = comparators(wl)
+        log("bench: other sizes")
+        extras["more_sizes"] = more_sizes(wl)
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle on the host")
