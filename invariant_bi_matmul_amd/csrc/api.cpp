@@ -42,8 +42,8 @@ bi::AttnDims dims_of(const bi_attn_shape* s) {
 }
 
 size_t decode_ws_bytes(const bi_attn_shape* s, int64_t tokens, int64_t nsplit) {
-  return (size_t)tokens * (size_t)s->num_q_heads * (size_t)nsplit * (size_t)(s->head_dim + 2) *
-         sizeof(float);
+  return (size_t)tokens * (size_t)s->num_q_heads * (size_t)nsplit *
+         (size_t)bi::attn_rec_floats(s->head_dim) * sizeof(float);
 }
 
 }  // namespace

@@ -478,20 +478,22 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, bool live, bf16x8 (
   }
 }
 
-// Write one block's partial record (o[D], m, l) for a live column.
+// Write one block's partial record (o[D], m, l, pad) for a live column:
+// exactly STORES vector stores per wave (a live column always exists), which
+// the decode stream counts in its waits.
+template <int D>
+struct PartialRec {
+  static constexpr int FLOATS = attn_rec_floats(D);
+  static constexpr int STORES = KV<D>::DB + 1;
+};
 template <int D>
 __device__ __forceinline__ void store_partial(float* rec, const f32x4 (&o)[KV<D>::DB], float m,
                                               float l) {
   constexpr int DB = KV<D>::DB;
   const int qq = (threadIdx.x & (kWave - 1)) >> 4;
 #pragma unroll
-  for (int i = 0; i < DB; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) rec[16 * i + 4 * qq + t] = o[i][t];
-  if (qq == 0) {
-    rec[D] = m;
-    rec[D + 1] = l;
-  }
+  for (int i = 0; i < DB; ++i) *(f32x4*)(rec + 16 * i + 4 * qq) = o[i];
+  if (qq == 0) *(f32x2_t*)(rec + D) = f32x2_t{m, l};
 }
 
 // ---- append ------------------------------------------------------------------
@@ -536,7 +538,7 @@ __global__ __launch_bounds__(128) void kv_append_kernel(const uint16_t* __restri
 // private ring of 4 slots without a break: while a unit's last chunks are
 // computed, the next unit's first chunks are already loading; the next unit's
 // block-table pages are read, and its q is copied into LDS, one unit ahead.
-// Workspace record per (b, q head, s): o[D], m, l  (fp32).
+// Workspace record per (b, q head, s): o[D], m, l, 2 pad floats (fp32).
 constexpr int kDecodeRing = 4;  // divides the 16 chunk loads of a split
 constexpr int kMapSeqs = 256;   // batches up to this size get the balanced unit list
 
@@ -546,15 +548,16 @@ struct DecodeUnit {
   int g, b, s, key0, last;
 };
 
-template <int D>
+template <int D, int RING_ = kDecodeRing>
 struct StreamSrc {
-  static constexpr int RING = kDecodeRing;
+  static constexpr int RING = RING_;
   static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
   static constexpr int LOADS = SLOT / 1024;          // 1 KiB loads per chunk
   static constexpr int AHEAD = RING - 1;             // chunks in flight
   static constexpr int QLOADS = 16 * KV<D>::ROWB / 1024;  // q copy of the next unit
+  static constexpr int STORES = PartialRec<D>::STORES;    // previous unit's record
   static_assert(16 % RING == 0, "slots repeat every split");
-  static_assert(LOADS * (AHEAD - 1) + QLOADS <= 63, "vmcnt range");
+  static_assert(LOADS * (AHEAD - 1) + STORES + QLOADS <= 63, "vmcnt range");
   const uint16_t* kc;
   const uint16_t* vc;
   const uint8_t* ring;
@@ -562,6 +565,7 @@ struct StreamSrc {
   int nkv;
   DecodeUnit<D> cur, nxt;
   bool has_next;
+  bool first;  // the wave's first unit: no record stores precede its chunks
 
   // stream position G: chunk G of the current unit (G < 16) or chunk G-16 of
   // the next one; K chunks are 0..7, V chunks 8..15
@@ -598,14 +602,21 @@ struct StreamSrc {
     }
   }
   __device__ __forceinline__ void prologue() const { prologue_from<0>(); }
-  // Before chunk IDX of the current unit is read: wait for it (the loads
-  // issued after it are the next AHEAD-1 stream chunks, plus the next unit's
-  // q copy while IDX < AHEAD), then refill the slot of chunk IDX-1.
+  // Before chunk IDX of the current unit is read: wait for it, then refill
+  // the slot of chunk IDX-1.  The operations issued after chunk IDX are the
+  // next AHEAD-1 stream chunks and, while IDX < AHEAD, the previous unit's
+  // record stores (unless this is the wave's first unit) and the next unit's
+  // q copy.  Without a next unit the wait counts only the chunks that follow
+  // (waiting for more is never wrong).
   template <int IDX>
   __device__ __forceinline__ void step() const {
     if (has_next) {
-      if constexpr (IDX < AHEAD) wait_vmcnt_le<LOADS * (AHEAD - 1) + QLOADS>();
-      else wait_vmcnt_le<LOADS * (AHEAD - 1)>();
+      if constexpr (IDX < AHEAD) {
+        if (first) wait_vmcnt_le<LOADS * (AHEAD - 1) + QLOADS>();
+        else wait_vmcnt_le<LOADS * (AHEAD - 1) + STORES + QLOADS>();
+      } else {
+        wait_vmcnt_le<LOADS * (AHEAD - 1)>();
+      }
       lds_reads_done();
       issue<IDX + AHEAD>();
     } else {
@@ -657,18 +668,18 @@ __device__ __forceinline__ void read_q(const uint8_t* slot, bf16x8 (&qf)[KV<D>::
     qf[t] = as_bf16x8(*(const u32x4*)(slot + col * KV<D>::ROWB + (((4 * t + q4) ^ qswz<D>(col)) << 4)));
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
+template <int D, int WAVES, int RING>
+__global__ __launch_bounds__(64 * WAVES) void bi_attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
     int smax, float c2) {
-  using Src = StreamSrc<D>;
+  using Src = StreamSrc<D, RING>;
   constexpr int QSLOT = 16 * KV<D>::ROWB;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[4][Src::RING * Src::SLOT + 2 * QSLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES][Src::RING * Src::SLOT + 2 * QSLOT];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t NW = (int64_t)gridDim.x * 4;
+  const int64_t NW = (int64_t)gridDim.x * WAVES;
   const int64_t total = (int64_t)B * nkv * smax;
   const int group = nq / nkv;
   const uint8_t* ring = lds[wave];
@@ -740,11 +751,11 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
     un.sp.load(bt + (int64_t)un.b * max_pages, un.key0, un.last);
   };
 
-  int64_t u = next_valid((int64_t)blockIdx.x * 4 + wave);
+  int64_t u = next_valid((int64_t)blockIdx.x * WAVES + wave);
   if (u >= total_units) return;
   ChunkLaneOffs<D> offs;
   offs.init();
-  Src src{kc, vc, ring, &offs, nkv, {}, {}, false};
+  Src src{kc, vc, ring, &offs, nkv, {}, {}, false, true};
   fill(src.cur, u);
   int qi = 0;
   copy_q<D>(q, src.cur.b, src.cur.g, nq, group, qslot0);
@@ -758,9 +769,19 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
       fill(src.nxt, un);
       copy_q<D>(q, src.nxt.b, src.nxt.g, nq, group, qslot0 + (uint32_t)(qi ^ 1) * QSLOT);
     }
-    // this unit's q copy is older than every chunk of the unit and than the
-    // next unit's q copy
-    wait_vmcnt_le<Src::LOADS * Src::AHEAD + Src::QLOADS>();
+    // Wait for this unit's q copy.  Issued after it: the unit's first AHEAD
+    // chunks, the previous unit's record stores (unless this is the wave's
+    // first unit) and the next unit's q copy (if there is a next unit).  The
+    // count is capped at the counter's range: a smaller count only waits longer.
+    constexpr int QA = Src::LOADS * Src::AHEAD;
+    constexpr int QB = QA + Src::STORES;
+    if (src.first) {
+      if (src.has_next) wait_vmcnt_le<QA + Src::QLOADS>();
+      else wait_vmcnt_le<QA>();
+    } else {
+      if (src.has_next) wait_vmcnt_le<(QB + Src::QLOADS < 63 ? QB + Src::QLOADS : 63)>();
+      else wait_vmcnt_le<(QB < 63 ? QB : 63)>();
+    }
     bf16x8 qf[1][KV<D>::DS];
     read_q<D>(ring + Src::RING * Src::SLOT + qi * QSLOT, qf[0]);
     const int L = src.cur.last + 1;
@@ -772,12 +793,13 @@ __global__ __launch_bounds__(256) void bi_attn_decode_partial_kernel(
     split_pv<D, 1>(src, p, o);
     if (live) {
       const int hq = src.cur.g * group + col;
-      store_partial<D>(ws + (((int64_t)src.cur.b * nq + hq) * smax + src.cur.s) * (D + 2), o[0],
+      store_partial<D>(ws + (((int64_t)src.cur.b * nq + hq) * smax + src.cur.s) * PartialRec<D>::FLOATS, o[0],
                        m[0], l[0]);
     }
     if (!src.has_next) break;
     u = un;
     src.cur = src.nxt;
+    src.first = false;
     qi ^= 1;
   }
   wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
@@ -799,14 +821,14 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
   const int d = threadIdx.x;
   const int L = kv_len[b];
   const int ns = min(smax, (L + split_len - 1) / split_len);
-  const float* rec = ws + bh * smax * (D + 2);
+  const float* rec = ws + bh * smax * PartialRec<D>::FLOATS;
   float m = rec[D], l = rec[D + 1], o = rec[d];
   for (int s0 = 1; s0 < ns; s0 += BATCH) {
     float pm[BATCH], pl[BATCH], po[BATCH];
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int s = min(s0 + j, ns - 1);
-      const float* rs = rec + (int64_t)s * (D + 2);
+      const float* rs = rec + (int64_t)s * PartialRec<D>::FLOATS;
       pm[j] = rs[D];
       pl[j] = rs[D + 1];
       po[j] = rs[d];
@@ -1053,7 +1075,8 @@ __global__ __launch_bounds__(256) void bix_attn_decode_splitkv_kernel(
       M = f.m;
     }
   }
-  if (live) store_partial<D>(ws + (((int64_t)b * nq + hq) * nsplit + sp) * (D + 2), O, M, Lsum);
+  if (live) store_partial<D>(ws + (((int64_t)b * nq + hq) * nsplit + sp) * PartialRec<D>::FLOATS, O,
+                            M, Lsum);
 }
 
 float base2_scale(float scale) { return scale * 1.44269504088896341f; }
@@ -1096,6 +1119,9 @@ hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* 
 
 // Workgroups of the persistent decode kernel: one per CU (each uses all of
 // a CU's LDS), fewer when there are fewer units.
+// Decode partial configuration: waves per workgroup and ring slots per wave
+// (one workgroup per CU uses the CU's LDS).
+constexpr int kDecodeWaves = 2, kDecodeSlots = 8;
 static int decode_workgroups(int64_t units) {
   static int cus = 0;
   if (cus == 0) {
@@ -1106,7 +1132,7 @@ static int decode_workgroups(int64_t units) {
     else
       cus = 256;
   }
-  const int64_t need = (units + 3) / 4;
+  const int64_t need = (units + kDecodeWaves - 1) / kDecodeWaves;
   return (int)(need < cus ? need : cus);
 }
 
@@ -1117,13 +1143,15 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* k
   const dim3 grid1((unsigned)decode_workgroups(units)), grid2((unsigned)((int64_t)s.B * s.nq));
   const float c2 = base2_scale(s.scale);
   if (s.d == 128) {
-    hipLaunchKernelGGL(bi_attn_decode_partial_kernel<128>, grid1, dim3(256), 0, st,
+    hipLaunchKernelGGL((bi_attn_decode_partial_kernel<128, kDecodeWaves, kDecodeSlots>), grid1,
+                       dim3(64 * kDecodeWaves), 0, st,
                        (const uint16_t*)q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
                        ws, s.B, s.nq, s.nkv, s.max_pages, max_splits, c2);
     hipLaunchKernelGGL(bi_attn_combine_kernel<128>, grid2, dim3(128), 0, st, (const float*)ws,
                        kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
   } else {
-    hipLaunchKernelGGL(bi_attn_decode_partial_kernel<64>, grid1, dim3(256), 0, st,
+    hipLaunchKernelGGL((bi_attn_decode_partial_kernel<64, kDecodeWaves, kDecodeSlots>), grid1,
+                       dim3(64 * kDecodeWaves), 0, st,
                        (const uint16_t*)q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
                        ws, s.B, s.nq, s.nkv, s.max_pages, max_splits, c2);
     hipLaunchKernelGGL(bi_attn_combine_kernel<64>, grid2, dim3(64), 0, st, (const float*)ws,

@@ -27,6 +27,9 @@ hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f3
 // ---- attention -------------------------------------------------------------
 constexpr int kSplit = 256;   // fixed key split
 constexpr int kPage = 16;     // tokens per page
+// Decode workspace record of one (sequence, q head, split): o[d], m, l and
+// two pad floats, so that every record starts on a 16-byte boundary.
+constexpr int attn_rec_floats(int d) { return d + 4; }
 
 struct AttnDims {
   int B, nq, nkv, d, max_pages;

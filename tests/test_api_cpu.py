@@ -83,7 +83,7 @@ def test_attention_validation(lib):
     import invariant_bi_matmul_amd as bi
     s = _shape()
     by = ctypes.byref
-    assert lib.bi_attn_workspace_bytes(by(s), 2, 300) == 2 * 32 * 2 * 130 * 4
+    assert lib.bi_attn_workspace_bytes(by(s), 2, 300) == 2 * 32 * 2 * 132 * 4
     assert lib.bi_attn_workspace_bytes(by(_shape(head_dim=96)), 2, 300) == 0
     args = [_p()] * 9 + [None]
     assert lib.bi_attn_prefill(by(_shape(head_dim=96)), *args, 10, 5, None) == UNSUP
