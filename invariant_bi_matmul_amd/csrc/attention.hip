@@ -180,7 +180,7 @@ __device__ __forceinline__ uint32_t dma_lane_off(int kfirst) {
 // of a split (KPI = 64 / chunks per row; all in the uniform page `page`) of
 // one kv head, swizzled for K or V, to LDS address lds_block.  Keys past
 // `last` read key `last` instead, so every value loaded is a written one.
-template <int D, bool IS_K>
+template <int D, bool IS_K, bool STREAM = false>
 __device__ __forceinline__ void dma_block(const uint16_t* pool, int page, int nkv, int g, int key0,
                                           int kfirst, int last, uint32_t lds_block) {
   constexpr int CPR = KV<D>::CPR;
@@ -191,7 +191,7 @@ __device__ __forceinline__ void dma_block(const uint16_t* pool, int page, int nk
   // the slot needs clamping
   const int slot = min(key0 + kl, last) & 15;
   const uint16_t* base = pool + ((int64_t)page * nkv + g) * 16 * D;
-  lds_dma16_sv(base, (uint32_t)(slot * D + logical * 8) * 2, lds_block);
+  lds_dma16_sv<STREAM>(base, (uint32_t)(slot * D + logical * 8) * 2, lds_block);
 }
 
 // LDS addresses of this lane's operand reads in chunk 0 of a K / V region
@@ -531,16 +531,18 @@ __global__ __launch_bounds__(128) void kv_append_kernel(const uint16_t* __restri
 }
 
 // ---- decode ------------------------------------------------------------------
-// Persistent: about one workgroup per CU, 4 waves.  Wave w of NW processes the
-// units u = w, w + NW, w + 2NW, ... of the dense enumeration (kv head g
-// fastest, then sequence b, then split s), skipping splits that start at or
-// past the sequence's length.  Each wave streams its units' chunks through a
-// private ring of 4 slots without a break: while a unit's last chunks are
-// computed, the next unit's first chunks are already loading; the next unit's
-// block-table pages are read, and its q is copied into LDS, one unit ahead.
+// Persistent: one workgroup per CU (fewer if there are fewer units) of
+// kDecodeWaves waves.  A unit is one (kv head g, sequence b, split s); wave w
+// of NW processes units w, w + NW, w + 2NW, ... of the list of existing units.
+// Each wave streams its units' chunks through a private ring of kDecodeSlots
+// LDS slots without a break: while a unit's last chunks are computed, the next
+// unit's first chunks are already loading; the next unit's block-table pages
+// are read, and its q is copied into LDS, one unit ahead.  Full splits load
+// their keys/values with the non-temporal hint (each byte is read once per
+// call).
 // Workspace record per (b, q head, s): o[D], m, l, 2 pad floats (fp32).
-constexpr int kDecodeRing = 4;  // divides the 16 chunk loads of a split
-constexpr int kMapSeqs = 256;   // batches up to this size get the balanced unit list
+constexpr int kDecodeWaves = 2, kDecodeSlots = 8;  // slots divide the 16 chunks of a split
+constexpr int kMapSeqs = 256;  // batches up to this size get the balanced unit list
 
 template <int D>
 struct DecodeUnit {
@@ -548,7 +550,7 @@ struct DecodeUnit {
   int g, b, s, key0, last;
 };
 
-template <int D, int RING_ = kDecodeRing>
+template <int D, int RING_>
 struct StreamSrc {
   static constexpr int RING = RING_;
   static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
@@ -583,7 +585,7 @@ struct StreamSrc {
       const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
       static_for<0, LOADS>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
-        lds_dma16_si<(G % RING) * SLOT + n * 1024>(
+        lds_dma16_si<(G % RING) * SLOT + n * 1024, true>(
             page_block(pool_g, un.sp.pg[(32 * CC + n * KPI) >> 4], page_elems),
             IS_K ? offs->k[n] : offs->v[n], ring0);
       });
@@ -591,6 +593,8 @@ struct StreamSrc {
     }
 #pragma unroll
     for (int n = 0; n < LOADS; ++n)
+      // the last split re-reads the last key for positions past the end:
+      // no streaming hint here, so those repeats hit in cache
       dma_block<D, IS_K>(pool, un.sp.pg[(32 * CC + n * KPI) >> 4], nkv, un.g, un.key0,
                          32 * CC + n * KPI, un.last, dst + (uint32_t)n * 1024);
   }
@@ -1117,11 +1121,8 @@ hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* 
   return hipGetLastError();
 }
 
-// Workgroups of the persistent decode kernel: one per CU (each uses all of
+// Workgroups of the persistent decode kernel: one per CU (each uses most of
 // a CU's LDS), fewer when there are fewer units.
-// Decode partial configuration: waves per workgroup and ring slots per wave
-// (one workgroup per CU uses the CU's LDS).
-constexpr int kDecodeWaves = 2, kDecodeSlots = 8;
 static int decode_workgroups(int64_t units) {
   static int cus = 0;
   if (cus == 0) {

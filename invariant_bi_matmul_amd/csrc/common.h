@@ -83,6 +83,10 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
 }
 // The same load with a wave-uniform 64-bit base (scalar registers) plus a
 // 32-bit per-lane byte offset, so a lane's address costs one register.
+// STREAM sets the non-temporal hint: for data read once per call (the decode
+// key/value stream), so that it does not displace lines the caches keep for
+// reuse; data that is re-read (prefill, matmul operands) leaves it off.
+template <bool STREAM = false>
 __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
   const uint64_t b = (uint64_t)(uintptr_t)sbase;
@@ -90,24 +94,36 @@ __device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, u
   const uint64_t ub =
       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m0v), "v"(voff), "s"(ub)
-               : "memory", "m0");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(ub)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(ub)
+                 : "memory", "m0");
 }
 // The same load to LDS address m0base + IMM (m0base wave-uniform): M0 is
 // formed by one scalar add inside the asm.
-template <int IMM>
+template <int IMM, bool STREAM = false>
 __device__ __forceinline__ void lds_dma16_si(const void* sbase, uint32_t voff, uint32_t m0base) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(m0base);
   const uint64_t b = (uint64_t)(uintptr_t)sbase;
   const uint64_t ub =
       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(m), "v"(voff), "s"(ub), "n"(IMM)
-               : "memory", "m0", "scc");
+  if constexpr (STREAM)
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(m), "v"(voff), "s"(ub), "n"(IMM)
+                 : "memory", "m0", "scc");
+  else
+    asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m), "v"(voff), "s"(ub), "n"(IMM)
+                 : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 // Make the compiler wait for a value's load here (an empty asm that reads
