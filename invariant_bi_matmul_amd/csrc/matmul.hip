@@ -54,7 +54,6 @@ struct Tile {
   static constexpr int LOADS = A_LOADS + W_LOADS;
   static constexpr int A_ROW = BK * 2, W_ROW = BN * 2;
   static constexpr int A_CPR = BK / 8, W_CPR = BN / 8;  // 16-byte chunks per row
-  static constexpr int LOADS_PER_STEP = (LOADS + KS - 2) / (KS - 1);
   static constexpr int GROUP_M = 8;                   // row-tiles per raster group
   static_assert(BK == 64, "swizzles assume 128-byte A rows");
   static_assert(BN >= 128, "W swizzle needs 16 chunks per k row");
@@ -133,7 +132,45 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   const int wave_m = wave / T::WAVES_N, wave_n = wave % T::WAVES_N;
 
   // Epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4.
+  // bf16 output: the four lanes of a quad hold four adjacent columns of the
+  // same four rows.  Two lane exchanges inside the quad (xor 1, then xor 2)
+  // transpose that 4x4 block of bf16 values, so that lane q holds row
+  // 2(q%2) + q/2 of it, four consecutive columns, stored as one 8-byte write
+  // (N is a multiple of 8, so the four columns are all in range or all out).
+  const int quad = lane & 3;
+  const int quad_row = 2 * (quad & 1) + (quad >> 1);
+  auto store_tile_bf16 = [&](int m0, int n0, const f32x16 (&acc)[MI][NI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = n0 + wave_n * T::WN + ni * 32 + ((lane & 31) & ~3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t p01 = pack_bf16x2(acc[mi][ni][4 * j], acc[mi][ni][4 * j + 1]);
+          const uint32_t p23 = pack_bf16x2(acc[mi][ni][4 * j + 2], acc[mi][ni][4 * j + 3]);
+          // xor 1: even lanes keep rows 0,1 and take the odd partner's; odd
+          // lanes keep rows 2,3 and take the even partner's
+          const uint32_t own = (quad & 1) ? p23 : p01;
+          const uint32_t got = (uint32_t)__builtin_amdgcn_mov_dpp((int)((quad & 1) ? p01 : p23),
+                                                                  0xB1, 0xF, 0xF, false);
+          const uint32_t x = (quad & 1) ? pack_lo(got, own) : pack_lo(own, got);
+          const uint32_t y = (quad & 1) ? pack_hi(got, own) : pack_hi(own, got);
+          // xor 2: lanes 0,1 keep their first row, lanes 2,3 their second
+          const uint32_t got2 =
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)((quad & 2) ? x : y), 0x4E, 0xF, 0xF, false);
+          const u32x2 v = (quad & 2) ? u32x2{got2, y} : u32x2{x, got2};
+          const int row = m0 + wave_m * T::WM + mi * 32 + 8 * j + 4 * (lane >> 5) + quad_row;
+          if (row < M && col < N) *(u32x2*)((uint16_t*)C + (int64_t)row * N + col) = v;
+        }
+      }
+    }
+  };
   auto store_tile = [&](int m0, int n0, const f32x16 (&acc)[MI][NI]) __attribute__((always_inline)) {
+    if (!SPLIT && !out_f32) {
+      store_tile_bf16(m0, n0, acc);
+      return;
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -147,10 +184,8 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
             const float v = acc[mi][ni][r];
             if (SPLIT) {
               ((float*)C)[(int64_t)blockIdx.z * M * N + o] = v;
-            } else if (out_f32) {
-              ((float*)C)[o] = v;
             } else {
-              ((uint16_t*)C)[o] = (uint16_t)f32_to_bf16(v);
+              ((float*)C)[o] = v;
             }
           }
         }
@@ -273,40 +308,55 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   int ckt = 0;      // its k-tiles done
   int cm0, cn0;
   raster_tile(first, tiles_m, tiles_n, cm0, cn0);
-  // One k-tile held in stage S: at most STAGES-2 younger k-tiles may still be
-  // loading when it is needed.
+  // One k-tile j held in stage S.  Its step-0 fragments were read during the
+  // previous k-tile's last step.  Steps 0..KS-2 read the next step's
+  // fragments under their MFMAs and issue load groups 1.. of k-tile j+2 (into
+  // the stage of j-1, free since the barrier before j-1's last step).  Before
+  // the last step every wave waits for its own loads of k-tile j+1; the
+  // barrier publishes it and ends every read of stage S, so the last step's
+  // MFMAs run under the reads of j+1's step 0, and group 0 of k-tile j+3 goes
+  // out into stage S at once.
   bf16x8 fa[2][MI], fb[2][NI];
+  constexpr int GRP = (T::LOADS + KS - 1) / KS;  // loads per group
+  auto issue_group = [&](int stage, int g) __attribute__((always_inline)) {
+    issue(stage, g * GRP, min((g + 1) * GRP, T::LOADS));
+  };
   auto ktile = [&](auto sc) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value;
     const uint8_t* Sp = smem + S * STAGE;
-    wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
-    __syncthreads();  // k-tile visible; every wave is done with the previous stage
+    const uint8_t* Snext = smem + ((S + 1) % STAGES) * STAGE;
     constexpr int sn = (S + STAGES - 1) % STAGES;
-    frags(Sp, 0, fa[0], fb[0]);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
-      if (kk + 1 < KS) frags(Sp, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      if (kk + 1 < KS) {
+        frags(Sp, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      } else {
+        wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
+        __syncthreads();  // next k-tile visible; every wave is done with this stage
+        __builtin_amdgcn_sched_barrier(0);
+        frags(Snext, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = mfma32(fa[kk & 1][mi], fb[kk & 1][ni], acc[mi][ni]);
-      if (kk + 1 < KS) {
-        // the next step's reads interleaved one for one with this step's MFMAs
+      // the next reads interleaved one for one with this step's MFMAs
 #pragma unroll
-        for (int i = 0; i < MI * NI; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        }
+      for (int i = 0; i < MI * NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KS) {
-        issue(sn, kk * T::LOADS_PER_STEP, min((kk + 1) * T::LOADS_PER_STEP, T::LOADS));
-        __builtin_amdgcn_sched_barrier(0);
+        issue_group(sn, kk + 1);
+        if (kk + 2 == KS) advance();
+      } else {
+        issue_group(S, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    advance();
     if (++ckt == nk) {  // the tile is complete
       store_tile(cm0, cn0, acc);
 #pragma unroll
@@ -323,6 +373,12 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
     issue(s, 0, T::LOADS);
     advance();
   }
+  // the first k-tile: wait for it, publish it, read its step 0; stage 2 is
+  // free, so group 0 of k-tile 2 goes out
+  wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
+  __syncthreads();
+  frags(smem, 0, fa[0], fb[0]);
+  issue_group(STAGES - 1, 0);
   static_assert(STAGES == 3, "the loop below is unrolled by the ring depth");
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
