@@ -75,15 +75,6 @@ struct KV {
   using vrow = std::conditional_t<D == 128, u32x4, u32x2>;  // DB dims of one key
 };
 
-// Calls f(integral_constant<int, i>) for i = I .. N-1.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // In-chunk key of the S^T A-operand row this lane loads for half h.
 __device__ __forceinline__ int okey_k(int h, int r) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 

@@ -22,15 +22,16 @@
 // four k rows a 32-lane half reads fall on four different block positions and
 // every transposing read is conflict-free.
 //
-// Schedule: one barrier per k-tile publishes tile k and frees the stage read
-// in tile k-1, which is refilled with tile k+2; the refill's loads are issued
-// in small groups after the MFMAs of each k-step, so the vector memory unit
-// never holds up a wave that has MFMAs to issue.  Fragments of k-step kk+1 are
-// read while the MFMAs of step kk run.  The ring is unrolled by its depth so
-// that every LDS address is a per-thread constant plus an immediate.
-// Workgroups are placed XCD-contiguously and walk groups of 8 row-tiles
-// (row-tiles fastest, then columns), so the workgroups resident on one XCD
-// share a compact block of A rows and W columns in that XCD's L2.
+// Schedule: one barrier per k-tile, placed before the last k-step of k-tile
+// k, publishes k-tile k+1 and frees k-tile k's stage.  Fragments of every
+// k-step are read while the previous step's MFMAs run (across the barrier
+// too), and the refill loads are issued in small groups after the MFMAs of
+// each k-step, so the vector memory unit never holds up a wave that has MFMAs
+// to issue.  The ring is unrolled by its depth so that every LDS address is a
+// per-thread constant plus an immediate.  Workgroups are placed
+// XCD-contiguously and walk groups of 4 row-tiles (row-tiles fastest, then
+// columns), so the 32 workgroups resident on one XCD share a 4 x 8 block of A
+// rows and W columns in that XCD's L2.
 //
 // bix_matmul_* is the non-invariant comparator from the problem column of the
 // same row: split-K with a split count chosen from the grid size (so from M),
@@ -54,7 +55,7 @@ struct Tile {
   static constexpr int LOADS = A_LOADS + W_LOADS;
   static constexpr int A_ROW = BK * 2, W_ROW = BN * 2;
   static constexpr int A_CPR = BK / 8, W_CPR = BN / 8;  // 16-byte chunks per row
-  static constexpr int GROUP_M = 8;                   // row-tiles per raster group
+  static constexpr int GROUP_M = 4;                   // row-tiles per raster group
   static_assert(BK == 64, "swizzles assume 128-byte A rows");
   static_assert(BN >= 128, "W swizzle needs 16 chunks per k row");
   static_assert(A_LOADS * NT * 16 == A_BYTES && W_LOADS * NT * 16 == W_BYTES, "tile/threads");
