@@ -368,6 +368,69 @@ def calibrate_copy(nbytes=1 << 30):
     print(json.dumps({"copy_bytes_each_way": nbytes, "launches": 3}))
 
 
+def e2e_llama8b(steps: int = 128):
+    """The whole stack end to end: a Llama-3-8B-shaped dense decoder (32 layers,
+    hidden 4096, GQA 32/8, SwiGLU 14336, vocab 128256, random-init weights) run
+    on the library's kernels.  A 256-token random prompt is decoded greedily
+    for ``steps`` tokens alone and among 63 other random prompts (lengths
+    U{64..512}); its tokens and logits are compared bit for bit.  The same is
+    done with the non-invariant comparator kernels.  ``unique_outputs`` counts
+    the distinct token sequences the probe gets over batches of 1, 4, 16 and 64
+    (the news.hada.io page's GPT-4 experiment counted unique outputs over
+    repeated calls).  Wall times include Python's launch overhead (about 400 library
+    calls per forward)."""
+    import torch
+    import synth
+    from invariant_bi_matmul_amd.model import Decoder, LlamaConfig
+    cfg = LlamaConfig()
+    w = synth.llama_weights(cfg.hidden, cfg.layers, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn,
+                            cfg.vocab, seed=0)
+    probe = synth.token_ids(256, cfg.vocab, 0, "e2e.probe")
+    lens = synth.stream(0, "e2e.lens").integers(64, 513, size=63).tolist()
+    others = [(i + 1, synth.token_ids(L, cfg.vocab, 0, "e2e.c%d" % i)) for i, L in enumerate(lens)]
+    cap = 64 * (512 + steps) + 64
+
+    def batch_of(n):
+        b = dict(others[:(n - 1) // 2])
+        b[0] = probe
+        b.update(others[(n - 1) // 2:n - 1])
+        return b
+
+    def differs(a, b):
+        return next((i for i, (x, y) in enumerate(zip(a, b)) if x != y), None)
+
+    out = {"config": {"layers": cfg.layers, "hidden": cfg.hidden, "n_q": cfg.n_q,
+                      "n_kv": cfg.n_kv, "ffn": cfg.ffn, "vocab": cfg.vocab,
+                      "rope_theta": cfg.rope_theta, "prompt": 256, "companions": 63,
+                      "steps": steps}}
+    for name, comp in (("invariant", False), ("comparator", True)):
+        dec = Decoder(cfg, w, max_tokens=cap, comparator=comp)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a_tok, a_log = dec.generate({0: probe}, steps, keep_logits=[0])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        b_tok, b_log = dec.generate(batch_of(64), steps, keep_logits=[0])
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        same = [torch.equal(x.view(torch.int32), y.view(torch.int32))
+                for x, y in zip(a_log[0], b_log[0])]
+        uniq = {tuple(a_tok[0]), tuple(b_tok[0])}
+        for n in (4, 16):
+            uniq.add(tuple(dec.generate(batch_of(n), steps)[0][0]))
+        out[name] = {"alone_s": t1 - t0, "batched64_s": t2 - t1,
+                     "batched64_tokens_per_s": 64 * steps / (t2 - t1),
+                     "tokens_equal": a_tok[0] == b_tok[0],
+                     "logits_bitwise_equal": all(same),
+                     "first_differing_token": differs(a_tok[0], b_tok[0]),
+                     "first_differing_logits_step": next((i for i, s in enumerate(same)
+                                                          if not s), None),
+                     "unique_outputs_over_batches_1_4_16_64": len(uniq)}
+        del dec, a_log, b_log
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +439,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the comparator timings and the invariance check")
+    ap.add_argument("--no-e2e", action="store_true",
+                    help="skip the end-to-end Llama-8B-shaped invariance run")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -416,6 +481,9 @@ def main():
         extras["cost_of_invariance"] = comparators(wl)
         log("bench: other sizes")
         extras["more_sizes"] = more_sizes(wl)
+        if not args.no_e2e:
+            log("bench: end-to-end Llama-8B-shaped stack, alone vs 63 companions")
+            extras["e2e_llama8b"] = e2e_llama8b()
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle on the host")

@@ -204,6 +204,46 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
                             int32_t max_kv_len, int32_t num_splits, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ---- Decoder-stack element-wise operations ---------------------------------
+ * The rest of a dense Llama-style decoder layer around the three kernels
+ * above, so that a whole stack can be run and its greedy output checked.  The
+ * news.hada.io page on GPT-4's output varying at temperature 0 (its problem
+ * statement) notes that greedy decoding of a dense decoder should be exactly
+ * reproducible, the next-token logits being a function of the input sequence
+ * and the weights alone; the operations below keep that per sequence.  The
+ * pages define none of them: they are the standard Llama forms.  Each output
+ * element depends only on its own row (and position), through one fixed fp32
+ * sequence, so each is batch-invariant by construction. */
+
+/* out[t, :] = table[ids[t], :].  ids int32 [tokens] (device; entries outside
+ * [0, vocab) are clamped into it); table bf16 [vocab, hidden]; out bf16
+ * [tokens, hidden].  hidden % 8 == 0.  Also a plain row gather. */
+int bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, int64_t hidden,
+             int64_t vocab, void* stream);
+
+/* Rotary position embedding in place, "rotate half" pairing: for token t at
+ * position p = pos[t], every head of q (bf16 [tokens, n_q, head_dim]) and of
+ * k (bf16 [tokens, n_kv, head_dim]), and i < head_dim/2, with a = x[i],
+ * b = x[i + head_dim/2] and angle = p * theta^(-2i/head_dim) (fp32):
+ *   x[i] = bf16(a cos - b sin),  x[i + head_dim/2] = bf16(a sin + b cos).
+ * head_dim even and <= 256; theta > 1.  q or k may be NULL when n_q or n_kv
+ * is 0.  pos int32 [tokens] (device). */
+int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, int32_t n_kv,
+            int32_t head_dim, float theta, void* stream);
+
+/* out = bf16(silu(gate) * up) element-wise, silu(g) = g / (1 + e^-g) in fp32.
+ * gate, up, out bf16 [n], n % 8 == 0; out may alias gate or up. */
+int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream);
+
+/* out = bf16(a + b) element-wise (the residual add).  bf16 [n], n % 8 == 0;
+ * out may alias a or b. */
+int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
+
+/* Greedy sampling: out[r] = the index of the largest of x[r, 0..n-1] (fp32
+ * [rows, n], 4-byte aligned), the lowest such index on ties.  NaN is never
+ * chosen; a row holding no number gives 0.  out int32 [rows]. */
+int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,7 @@ __all__ = [
     "BIError", "lib_path", "load", "abi_version", "rmsnorm", "matmul", "attn_workspace_bytes",
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
+    "embed", "rope", "swiglu", "add", "argmax",
 ]
 
 SPLIT = 256
@@ -79,6 +80,11 @@ def load():
         "bix_attn_decode_workspace_bytes": (sz, [SP, i32, i32]),
         "bix_attn_decode_splitkv": (ctypes.c_int,
                                     [SP, P, P, P, P, P, P, P, P, P, i32, i32, P, sz, P]),
+        "bi_embed": (ctypes.c_int, [P, P, P, i64, i64, i64, P]),
+        "bi_rope": (ctypes.c_int, [P, P, P, i64, i32, i32, i32, f32, P]),
+        "bi_swiglu": (ctypes.c_int, [P, P, P, i64, P]),
+        "bi_add": (ctypes.c_int, [P, P, P, i64, P]),
+        "bi_argmax": (ctypes.c_int, [P, P, i64, i64, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -313,3 +319,62 @@ def bix_attn_decode_splitkv(q, k_new, v_new, kv_len, block_table, k_cache, v_cac
         _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(max_kv_len), int(num_splits),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return (o, lse) if lse is not None else o
+
+
+# --------------------------------------------------------------------------- decoder stack
+
+def embed(ids: torch.Tensor, table: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """out[t] = table[ids[t]] (ids clamped into range); ids int32 [T], table bf16 [V, H]."""
+    _dev(ids, "ids", torch.int32)
+    _dev(table, "table", torch.bfloat16)
+    if ids.dim() != 1 or table.dim() != 2:
+        raise ValueError("need ids [T] and table [V, H]")
+    T, (V, H) = ids.shape[0], table.shape
+    o = torch.empty(T, H, dtype=torch.bfloat16, device=table.device) if out is None else \
+        _dev(out, "out", torch.bfloat16, (T, H))
+    _check("bi_embed", load().bi_embed(_ptr(ids), _ptr(table), _ptr(o), T, H, V, _stream()))
+    return o
+
+
+def rope(q: torch.Tensor, k: torch.Tensor, pos: torch.Tensor, theta: float):
+    """Rotary embedding in place ("rotate half"); q bf16 [T, n_q, d], k bf16
+    [T, n_kv, d], pos int32 [T].  Returns (q, k)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(k, "k", torch.bfloat16)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("need q [T, n_q, d] and k [T, n_kv, d]")
+    T, nq, d = q.shape
+    _dev(pos, "pos", torch.int32, (T,))
+    _check("bi_rope", load().bi_rope(_ptr(q), _ptr(k), _ptr(pos), T, nq, k.shape[1], d,
+                                     float(theta), _stream()))
+    return q, k
+
+
+def swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """bf16(silu(gate) * up), same shape as gate."""
+    _dev(gate, "gate", torch.bfloat16)
+    _dev(up, "up", torch.bfloat16, gate.shape)
+    o = torch.empty_like(gate) if out is None else _dev(out, "out", torch.bfloat16, gate.shape)
+    _check("bi_swiglu", load().bi_swiglu(_ptr(gate), _ptr(up), _ptr(o), gate.numel(), _stream()))
+    return o
+
+
+def add(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """bf16(a + b); ``out`` may be ``a``."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(b, "b", torch.bfloat16, a.shape)
+    o = torch.empty_like(a) if out is None else _dev(out, "out", torch.bfloat16, a.shape)
+    _check("bi_add", load().bi_add(_ptr(a), _ptr(b), _ptr(o), a.numel(), _stream()))
+    return o
+
+
+def argmax(x: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Row-wise argmax of fp32 [rows, n] (lowest index on ties); int32 [rows]."""
+    _dev(x, "x", torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, n]")
+    rows, n = x.shape
+    o = torch.empty(rows, dtype=torch.int32, device=x.device) if out is None else \
+        _dev(out, "out", torch.int32, (rows,))
+    _check("bi_argmax", load().bi_argmax(_ptr(x), _ptr(o), rows, n, _stream()))
+    return o

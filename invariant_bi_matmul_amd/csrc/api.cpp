@@ -289,4 +289,77 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
   }
 }
 
+// ---- decoder-stack element-wise operations -----------------------------------
+
+int bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, int64_t hidden,
+             int64_t vocab, void* stream) {
+  try {
+    if (tokens < 0 || hidden < 0 || vocab < 0) return BI_ERR_INVALID_SHAPE;
+    if (tokens == 0 || hidden == 0) return BI_OK;
+    if (vocab == 0 || hidden % 8 != 0) return BI_ERR_INVALID_SHAPE;
+    if (tokens > kMaxGridX) return BI_ERR_UNSUPPORTED;
+    if (ids == nullptr || table == nullptr || out == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned4(ids) || !aligned16(table) || !aligned16(out)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_embed(ids, table, out, tokens, hidden, vocab, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, int32_t n_kv,
+            int32_t head_dim, float theta, void* stream) {
+  try {
+    if (tokens < 0 || n_q < 0 || n_kv < 0) return BI_ERR_INVALID_SHAPE;
+    if (tokens == 0 || n_q + n_kv == 0) return BI_OK;
+    if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return BI_ERR_INVALID_SHAPE;
+    if (!(theta > 1.0f) || !isfinite(theta)) return BI_ERR_INVALID_SHAPE;
+    if (tokens > kMaxGridX || (int64_t)n_q + n_kv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
+    if (pos == nullptr || (n_q > 0 && q == nullptr) || (n_kv > 0 && k == nullptr))
+      return BI_ERR_NULL_POINTER;
+    if (!aligned4(pos)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(
+        bi::launch_rope(q, k, pos, tokens, n_q, n_kv, head_dim, theta, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream) {
+  try {
+    if (n < 0 || n % 8 != 0) return BI_ERR_INVALID_SHAPE;
+    if (n == 0) return BI_OK;
+    if (gate == nullptr || up == nullptr || out == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(gate) || !aligned16(up) || !aligned16(out)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_swiglu(gate, up, out, n, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
+  try {
+    if (n < 0 || n % 8 != 0) return BI_ERR_INVALID_SHAPE;
+    if (n == 0) return BI_OK;
+    if (a == nullptr || b == nullptr || out == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_add(a, b, out, n, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream) {
+  try {
+    if (rows < 0 || n < 0) return BI_ERR_INVALID_SHAPE;
+    if (rows == 0) return BI_OK;
+    if (n == 0 || n > 0x7ffffffe) return BI_ERR_INVALID_SHAPE;
+    if (rows > kMaxGridX) return BI_ERR_UNSUPPORTED;
+    if (x == nullptr || out == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned4(x) || !aligned4(out)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_argmax(x, out, rows, n, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
 }  // extern "C"

@@ -52,4 +52,13 @@ hipError_t launch_attn_decode_splitkv(const AttnDims& s, const void* q, const in
                                       hipStream_t st);
 int attn_splitkv_auto(int B, int nkv, int max_kv_len);
 
+// ---- decoder-stack element-wise operations (model.hip) ----------------------
+hipError_t launch_embed(const int32_t* ids, const void* table, void* out, int64_t tokens,
+                        int64_t hidden, int64_t vocab, hipStream_t st);
+hipError_t launch_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int nq, int nkv,
+                       int d, float theta, hipStream_t st);
+hipError_t launch_swiglu(const void* gate, const void* up, void* out, int64_t n, hipStream_t st);
+hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStream_t st);
+hipError_t launch_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, hipStream_t st);
+
 }  // namespace bi

@@ -322,8 +322,40 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   auto issue_group = [&](int stage, int g) __attribute__((always_inline)) {
     issue(stage, g * GRP, min((g + 1) * GRP, T::LOADS));
   };
-  auto ktile = [&](auto sc) __attribute__((always_inline)) {
-    constexpr int S = decltype(sc)::value;
+  // Rows past M are never stored, and MFMA rows do not interact, so when every
+  // tile is the single row-tile (M <= BM), the MFMAs (and A reads) of a wave's
+  // 32-row blocks that hold no row below M are skipped: the kernel runs the
+  // variant with this wave's LIVE blocks throughout.  A row's bits stay those
+  // of the full tile (same instruction, same k order); at small M the tile
+  // then streams W instead of computing padding.
+  static_assert(MI == 2, "the live-block variants assume two 32-row blocks per wave");
+  int live = MI;
+  if (tiles_m == 1) {
+    const int rows = M - wave_m * T::WM;
+    live = __builtin_amdgcn_readfirstlane(rows <= 0 ? 0 : (rows >= MI * 32 ? MI : (rows + 31) / 32));
+  }
+  // the fragments of step kk for the first LIVE row blocks (all of B if any)
+  auto frags_live = [&](const uint8_t* S, int kk, bf16x8 (&af)[MI], bf16x8 (&bw)[NI],
+                        auto lc) __attribute__((always_inline)) {
+    constexpr int LIVE = decltype(lc)::value;
+    if constexpr (LIVE == MI) {
+      frags(S, kk, af, bw);
+    } else if constexpr (LIVE > 0) {
+#pragma unroll
+      for (int mi = 0; mi < LIVE; ++mi) af[mi] = as_bf16x8(*(const u32x4*)(S + ao[kk][mi]));
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        s16x4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(S + wo[ni] + (16 * kk + 4 * h) * T::W_ROW));
+        bw[ni] = join_tr(v[0], v[1]);
+      }
+    }
+  };
+  auto ktile_body = [&](auto sc, auto lc) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value, LIVE = decltype(lc)::value;
     const uint8_t* Sp = smem + S * STAGE;
     const uint8_t* Snext = smem + ((S + 1) % STAGES) * STAGE;
     constexpr int sn = (S + STAGES - 1) % STAGES;
@@ -331,21 +363,22 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
     for (int kk = 0; kk < KS; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KS) {
-        frags(Sp, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        frags_live(Sp, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], lc);
       } else {
         wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
         __syncthreads();  // next k-tile visible; every wave is done with this stage
         __builtin_amdgcn_sched_barrier(0);
+        // all of them: the next k-tile may start a tile with more live rows
         frags(Snext, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
       }
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < LIVE; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
           acc[mi][ni] = mfma32(fa[kk & 1][mi], fb[kk & 1][ni], acc[mi][ni]);
       // the next reads interleaved one for one with this step's MFMAs
 #pragma unroll
-      for (int i = 0; i < MI * NI; ++i) {
+      for (int i = 0; i < LIVE * NI; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
@@ -358,6 +391,9 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto ktile = [&](auto sc, auto lc) __attribute__((always_inline)) {
+    ktile_body(sc, lc);
     if (++ckt == nk) {  // the tile is complete
       store_tile(cm0, cn0, acc);
 #pragma unroll
@@ -384,14 +420,22 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  int64_t p = 0;
-  for (; p + 3 <= total; p += 3) {
-    ktile(S0{});
-    ktile(S1{});
-    ktile(S2{});
-  }
-  if (p < total) ktile(S0{});
-  if (p + 1 < total) ktile(S1{});
+  auto run = [&](auto lc) __attribute__((always_inline)) {
+    int64_t p = 0;
+    for (; p + 3 <= total; p += 3) {
+      ktile(S0{}, lc);
+      ktile(S1{}, lc);
+      ktile(S2{}, lc);
+    }
+    if (p < total) ktile(S0{}, lc);
+    if (p + 1 < total) ktile(S1{}, lc);
+  };
+  if (live == MI)
+    run(std::integral_constant<int, MI>{});
+  else if (live == 1)
+    run(std::integral_constant<int, 1>{});
+  else
+    run(std::integral_constant<int, 0>{});
   wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
 }
 

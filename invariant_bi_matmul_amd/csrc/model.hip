@@ -1,0 +1,177 @@
+// Element-wise and per-row operations of a Llama-style decoder stack around
+// the three batch-invariant kernels: token embedding gather, rotary position
+// embedding, SwiGLU, residual add and greedy argmax.
+//
+// None of them reduces across rows: every output element depends only on its
+// own row's inputs (and, for the rotary embedding, on its position), through
+// one fixed sequence of fp32 operations.  So each is batch-invariant by
+// construction; the stack built from them and from RMSNorm, matmul and split-KV
+// attention gives a sequence the same tokens and logits alone or in any batch.
+//
+// Numerics: built with -ffp-contract=off and no fast-math (one rounding per
+// operation as written); bf16 results are rounded to nearest even by
+// pack_bf16x2.  The transcendental functions are the HIP device library's
+// sinf/cosf/powf/expf, called the same way for every element.
+#include <stdint.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace bi {
+namespace {
+
+constexpr int kElemThreads = 256;
+
+// out[t, :] = table[ids[t], :]; ids are clamped into [0, vocab).
+__global__ __launch_bounds__(kElemThreads) void embed_kernel(const int32_t* __restrict__ ids,
+                                                             const u32x4* __restrict__ table,
+                                                             u32x4* __restrict__ out,
+                                                             int64_t vocab, int chunks) {
+  const int64_t t = blockIdx.x;
+  int64_t id = ids[t];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  const u32x4* src = table + id * chunks;
+  u32x4* dst = out + t * chunks;
+  for (int c = threadIdx.x; c < chunks; c += kElemThreads) dst[c] = src[c];
+}
+
+// Rotary embedding, "rotate half" pairing: for head h of token t at position
+// p and i < d/2, with a = x[i], b = x[i + d/2] and angle = p * theta^(-2i/d):
+//   x[i] = a cos - b sin,  x[i + d/2] = a sin + b cos.
+// Grid (tokens, n_q + n_kv); thread i owns pair i.  In place.
+__global__ void rope_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                            const int32_t* __restrict__ pos, int nq, int nkv, int d,
+                            float theta) {
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int i = threadIdx.x;
+  const int half = d / 2;
+  if (i >= half) return;
+  uint16_t* x = h < nq ? q + (t * nq + h) * d : k + (t * nkv + (h - nq)) * d;
+  const float inv_freq = powf(theta, -(float)(2 * i) / (float)d);
+  const float angle = (float)pos[t] * inv_freq;
+  const float s = sinf(angle), c = cosf(angle);
+  const float a = bf16_to_f32(x[i]), b = bf16_to_f32(x[i + half]);
+  const float ya = a * c - b * s;
+  const float yb = a * s + b * c;
+  x[i] = (uint16_t)f32_to_bf16(ya);
+  x[i + half] = (uint16_t)f32_to_bf16(yb);
+}
+
+// out = bf16(silu(gate) * up), silu(g) = g / (1 + e^-g); eight elements per
+// thread.
+__global__ __launch_bounds__(kElemThreads) void swiglu_kernel(const u32x4* __restrict__ gate,
+                                                              const u32x4* __restrict__ up,
+                                                              u32x4* __restrict__ out,
+                                                              int64_t vecs) {
+  for (int64_t v = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; v < vecs;
+       v += (int64_t)gridDim.x * kElemThreads) {
+    const u32x4 g = gate[v], u = up[v];
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float r[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float gv = h ? bf16_hi(g[j]) : bf16_lo(g[j]);
+        const float uv = h ? bf16_hi(u[j]) : bf16_lo(u[j]);
+        const float silu = gv / (1.0f + expf(-gv));
+        r[h] = silu * uv;
+      }
+      o[j] = pack_bf16x2(r[0], r[1]);
+    }
+    out[v] = o;
+  }
+}
+
+// out = bf16(a + b); eight elements per thread.  out may alias a or b.
+__global__ __launch_bounds__(kElemThreads) void add_kernel(const u32x4* a, const u32x4* b,
+                                                           u32x4* out, int64_t vecs) {
+  for (int64_t v = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; v < vecs;
+       v += (int64_t)gridDim.x * kElemThreads) {
+    const u32x4 x = a[v], y = b[v];
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = pack_bf16x2(bf16_lo(x[j]) + bf16_lo(y[j]), bf16_hi(x[j]) + bf16_hi(y[j]));
+    out[v] = o;
+  }
+}
+
+// Greedy argmax of one fp32 row per workgroup: the largest value, the lowest
+// index among equal values; NaN is never chosen, and a row with no number in
+// it gives 0.  (value desc, index asc) is a total order on the candidates, so
+// the result does not depend on how the scan is split or reduced.
+struct Best {
+  float v;
+  int i;
+};
+__device__ __forceinline__ Best better(Best x, Best y) {
+  if (y.v > x.v || (y.v == x.v && y.i < x.i)) return y;
+  return x;
+}
+__global__ __launch_bounds__(kElemThreads) void argmax_kernel(const float* __restrict__ x,
+                                                              int32_t* __restrict__ out,
+                                                              int64_t n) {
+  const float* row = x + (int64_t)blockIdx.x * n;
+  Best b{-INFINITY, INT32_MAX};
+  for (int64_t j = threadIdx.x; j < n; j += kElemThreads) b = better(b, Best{row[j], (int)j});
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) {
+    const Best o{__shfl_xor(b.v, s), __shfl_xor(b.i, s)};
+    b = better(b, o);
+  }
+  __shared__ Best part[kElemThreads / kWave];
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) part[wave] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Best r = part[0];
+    for (int w = 1; w < kElemThreads / kWave; ++w) r = better(r, part[w]);
+    out[blockIdx.x] = r.i == INT32_MAX ? 0 : r.i;
+  }
+}
+
+unsigned elem_grid(int64_t vecs) {
+  int64_t g = (vecs + kElemThreads - 1) / kElemThreads;
+  if (g > 65536) g = 65536;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_embed(const int32_t* ids, const void* table, void* out, int64_t tokens,
+                        int64_t hidden, int64_t vocab, hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)tokens), dim3(kElemThreads), 0, st, ids,
+                     (const u32x4*)table, (u32x4*)out, vocab, (int)(hidden / 8));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int nq, int nkv,
+                       int d, float theta, hipStream_t st) {
+  const int threads = ((d / 2 + kWave - 1) / kWave) * kWave;
+  hipLaunchKernelGGL(rope_kernel, dim3((unsigned)tokens, (unsigned)(nq + nkv)), dim3(threads), 0,
+                     st, (uint16_t*)q, (uint16_t*)k, pos, nq, nkv, d, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const void* gate, const void* up, void* out, int64_t n, hipStream_t st) {
+  const int64_t vecs = n / 8;
+  hipLaunchKernelGGL(swiglu_kernel, dim3(elem_grid(vecs)), dim3(kElemThreads), 0, st,
+                     (const u32x4*)gate, (const u32x4*)up, (u32x4*)out, vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStream_t st) {
+  const int64_t vecs = n / 8;
+  hipLaunchKernelGGL(add_kernel, dim3(elem_grid(vecs)), dim3(kElemThreads), 0, st,
+                     (const u32x4*)a, (const u32x4*)b, (u32x4*)out, vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(kElemThreads), 0, st, x, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace bi

@@ -1,0 +1,244 @@
+"""A dense Llama-style decoder stack run on libbi's batch-invariant kernels.
+
+Every arithmetic step is a libbi call:
+- token embedding and row gathers: ``bi_embed``;
+- ``bi_rmsnorm``, then ``bi_matmul`` for the q/k/v, output, gate/up/down and
+  lm_head projections;
+- ``bi_rope``;
+- ``bi_attn_prefill`` / ``bi_attn_decode`` over a paged KV cache (16-token
+  pages, fixed 256-position splits, fixed-order combine);
+- ``bi_add`` (residual), ``bi_swiglu``, and ``bi_argmax`` (greedy sampling).
+
+This module keeps only bookkeeping: the weights, the KV pages each sequence
+owns, and the per-call index arrays (token ids, positions, cu_q, kv_len,
+block tables).  Since every kernel is batch-invariant, a sequence gets the
+same logits and tokens, bit for bit, whether it runs alone or among any
+other sequences, and however its prompt is chunked.  That is the end-to-end
+property the tests and ``bench.py`` check.
+
+The layer is the usual pre-norm one:
+  h = x + W_o attn(rope(W_q n1(x)), rope(W_k n1(x)), W_v n1(x))
+  y = h + W_down (silu(W_gate n2(h)) * W_up n2(h))
+with n1, n2 RMSNorm, GQA attention (n_q query heads over n_kv key/value
+heads) and softmax scale 1/sqrt(head_dim).  Then logits = W_lm n_f(x_last)
+in fp32 and the next token is their argmax (lowest index on ties).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import (PAGE, add, argmax, attn_decode, attn_prefill, attn_workspace_bytes,
+               bix_attn_decode_splitkv, bix_matmul_splitk, bix_rmsnorm_splitrow, embed,
+               make_shape, matmul, rmsnorm, rope, swiglu)
+
+__all__ = ["LlamaConfig", "LAYER_WEIGHTS", "weight_shapes", "Decoder"]
+
+
+@dataclass(frozen=True)
+class LlamaConfig:
+    """Llama-3-8B shape by default.  The pages name no vocabulary size or
+    rotary base; these are Llama 3's, and neither affects invariance."""
+    hidden: int = 4096
+    layers: int = 32
+    n_q: int = 32
+    n_kv: int = 8
+    head_dim: int = 128
+    ffn: int = 14336
+    vocab: int = 128256
+    rope_theta: float = 500000.0
+    eps: float = 1e-5
+
+
+LAYER_WEIGHTS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+
+
+def weight_shapes(cfg: LlamaConfig) -> Tuple[Dict[str, tuple], Dict[str, tuple]]:
+    """(shapes of the global weights, shapes of one layer's weights); every
+    projection is stored [in, out], the layout ``bi_matmul`` reads."""
+    H, F, V = cfg.hidden, cfg.ffn, cfg.vocab
+    qd, kvd = cfg.n_q * cfg.head_dim, cfg.n_kv * cfg.head_dim
+    glob = {"embed": (V, H), "final_norm": (H,), "lm_head": (H, V)}
+    layer = {"attn_norm": (H,), "wq": (H, qd), "wk": (H, kvd), "wv": (H, kvd), "wo": (qd, H),
+             "mlp_norm": (H,), "w_gate": (H, F), "w_up": (H, F), "w_down": (F, H)}
+    return glob, layer
+
+
+@dataclass
+class _Seq:
+    length: int = 0
+    pages: List[int] = field(default_factory=list)
+
+
+class Decoder:
+    """Holds the weights and a paged KV cache for up to ``max_tokens`` cached
+    positions in total; sequences are added, stepped and released by id.
+
+    ``comparator=True`` swaps in the library's non-invariant comparators
+    (split-row RMSNorm, split-K matmul and split-KV decode attention, whose
+    split counts follow the batch size), as a negative control: with them a
+    sequence's bits depend on its companions."""
+
+    def __init__(self, cfg: LlamaConfig, weights: dict, max_tokens: int,
+                 device: Optional[torch.device] = None, comparator: bool = False):
+        glob, layer = weight_shapes(cfg)
+        for name, shape in glob.items():
+            if tuple(weights[name].shape) != shape or weights[name].dtype != torch.bfloat16:
+                raise ValueError("weight %s must be bf16 %s" % (name, shape))
+        if len(weights["layers"]) != cfg.layers:
+            raise ValueError("need %d layers of weights" % cfg.layers)
+        for lw in weights["layers"]:
+            for name, shape in layer.items():
+                if tuple(lw[name].shape) != shape or lw[name].dtype != torch.bfloat16:
+                    raise ValueError("layer weight %s must be bf16 %s" % (name, shape))
+        self.cfg = cfg
+        self.w = weights
+        self.device = device or weights["embed"].device
+        self.num_pages = (max_tokens + PAGE - 1) // PAGE + 1
+        cache = (self.num_pages, cfg.n_kv, PAGE, cfg.head_dim)
+        self.kc = [torch.zeros(cache, dtype=torch.bfloat16, device=self.device)
+                   for _ in range(cfg.layers)]
+        self.vc = [torch.zeros(cache, dtype=torch.bfloat16, device=self.device)
+                   for _ in range(cfg.layers)]
+        self.free = list(range(self.num_pages - 1, -1, -1))
+        self.seqs: Dict[int, _Seq] = {}
+        self.scale = float(torch.tensor(1.0 / math.sqrt(cfg.head_dim), dtype=torch.float32))
+        self.comparator = comparator
+        if comparator:
+            self._norm = lambda x, g: bix_rmsnorm_splitrow(x, g, cfg.eps)
+            self._mm = lambda a, w, **kw: bix_matmul_splitk(a, w, **kw)
+        else:
+            self._norm = lambda x, g: rmsnorm(x, g, cfg.eps)
+            self._mm = matmul
+
+    # ---- KV page bookkeeping ---------------------------------------------------
+    def add_sequence(self, sid: int):
+        if sid in self.seqs:
+            raise ValueError("sequence %d exists" % sid)
+        self.seqs[sid] = _Seq()
+
+    def release(self, sid: int):
+        s = self.seqs.pop(sid)
+        self.free.extend(reversed(s.pages))
+
+    def length(self, sid: int) -> int:
+        return self.seqs[sid].length
+
+    def _reserve(self, s: _Seq, new_len: int):
+        need = (new_len + PAGE - 1) // PAGE
+        while len(s.pages) < need:
+            if not self.free:
+                raise RuntimeError("KV pool exhausted")
+            s.pages.append(self.free.pop())
+
+    # ---- one forward call ------------------------------------------------------
+    def forward(self, batch: Sequence[Tuple[int, Sequence[int]]]):
+        """Feed new tokens to sequences: ``batch`` lists (sequence id, new token
+        ids).  Returns (logits fp32 [B, vocab] at each sequence's last new
+        token, next tokens int32 [B] = their argmax).  A call in which every
+        sequence brings one token is a decode step (``bi_attn_decode``);
+        otherwise a (chunked) prefill (``bi_attn_prefill``)."""
+        cfg, dev = self.cfg, self.device
+        if not batch:
+            raise ValueError("empty batch")
+        seqs = [self.seqs[sid] for sid, _ in batch]
+        n_new = [len(ids) for _, ids in batch]
+        if min(n_new) < 1:
+            raise ValueError("every sequence needs at least one new token")
+        starts = [s.length for s in seqs]
+        after = [a + n for a, n in zip(starts, n_new)]
+        for s, L in zip(seqs, after):
+            self._reserve(s, L)
+        B, T = len(batch), sum(n_new)
+        maxp = max(len(s.pages) for s in seqs)
+        table = [s.pages + [s.pages[-1]] * (maxp - len(s.pages)) for s in seqs]
+        cu = [0]
+        for n in n_new:
+            cu.append(cu[-1] + n)
+        i32 = dict(dtype=torch.int32, device=dev)
+        ids = torch.tensor([t for _, toks in batch for t in toks], **i32)
+        pos = torch.tensor([p for a, n in zip(starts, n_new) for p in range(a, a + n)], **i32)
+        cu_q = torch.tensor(cu, **i32)
+        kv_len = torch.tensor(after, **i32)
+        bt = torch.tensor(table, **i32)
+        last = torch.tensor([c - 1 for c in cu[1:]], **i32)
+        decode = max(n_new) == 1
+        nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
+        ws = None
+        if decode and not self.comparator:
+            shape = make_shape(B, nq, nkv, d, maxp, self.num_pages, self.scale)
+            need = attn_workspace_bytes(shape, B, max(after))
+            ws = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=dev)
+        norm, mm = self._norm, self._mm
+
+        x = embed(ids, self.w["embed"])
+        for li, lw in enumerate(self.w["layers"]):
+            h = norm(x, lw["attn_norm"])
+            q = mm(h, lw["wq"]).view(T, nq, d)
+            k = mm(h, lw["wk"]).view(T, nkv, d)
+            v = mm(h, lw["wv"]).view(T, nkv, d)
+            rope(q, k, pos, cfg.rope_theta)
+            if decode and self.comparator:
+                o = bix_attn_decode_splitkv(q, k, v, kv_len, bt, self.kc[li], self.vc[li],
+                                            self.scale, max(after))
+            elif decode:
+                o = attn_decode(q, k, v, kv_len, bt, self.kc[li], self.vc[li], self.scale,
+                                max(after), workspace=ws)
+            else:
+                o = attn_prefill(q, k, v, cu_q, kv_len, bt, self.kc[li], self.vc[li], self.scale,
+                                 max(n_new))
+            add(x, mm(o.view(T, nq * d), lw["wo"]), out=x)
+            h = norm(x, lw["mlp_norm"])
+            g = mm(h, lw["w_gate"])
+            swiglu(g, mm(h, lw["w_up"]), out=g)
+            add(x, mm(g, lw["w_down"]), out=x)
+        xl = embed(last, x)  # the last new token of each sequence (a row gather)
+        logits = mm(norm(xl, self.w["final_norm"]), self.w["lm_head"], out_dtype=torch.float32)
+        nxt = argmax(logits)
+        for s, L in zip(seqs, after):
+            s.length = L
+        return logits, nxt
+
+    # ---- greedy generation -----------------------------------------------------
+    def generate(self, prompts: Dict[int, Sequence[int]], steps: int,
+                 chunk: Optional[int] = None, keep_logits: Sequence[int] = ()):
+        """Prefill every prompt (in one call, or in calls of ``chunk`` tokens per
+        sequence), then ``steps`` greedy decode steps over all of them.
+        Returns ({id: generated tokens}, {id: [fp32 logits per generated token]})
+        where logits are kept (on the device) only for ids in ``keep_logits``."""
+        for sid in prompts:
+            self.add_sequence(sid)
+        sids = list(prompts)
+        toks: Dict[int, List[int]] = {sid: [] for sid in sids}
+        kept: Dict[int, List[torch.Tensor]] = {sid: [] for sid in keep_logits}
+        off = {sid: 0 for sid in sids}
+        while True:
+            part = []
+            for sid in sids:
+                p = prompts[sid]
+                if off[sid] < len(p):
+                    n = len(p) - off[sid] if chunk is None else min(chunk, len(p) - off[sid])
+                    part.append((sid, list(p[off[sid]:off[sid] + n])))
+            if not part:
+                break
+            logits, nxt = self.forward(part)
+            nxt = nxt.tolist()
+            for i, (sid, ids) in enumerate(part):
+                off[sid] += len(ids)
+                if off[sid] == len(prompts[sid]):  # the prompt's last token: first output
+                    toks[sid].append(nxt[i])
+                    if sid in kept:
+                        kept[sid].append(logits[i].clone())
+        for _ in range(steps - 1):
+            logits, nxt = self.forward([(sid, [toks[sid][-1]]) for sid in sids])
+            nxt = nxt.tolist()
+            for i, sid in enumerate(sids):
+                toks[sid].append(nxt[i])
+                if sid in kept:
+                    kept[sid].append(logits[i].clone())
+        for sid in sids:
+            self.release(sid)
+        return toks, kept

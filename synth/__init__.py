@@ -196,3 +196,36 @@ def device_normal_bf16(shape, mean: float, std: float, seed: int, tag: str, devi
     t = torch.empty(shape, dtype=torch.float32, device=device)
     t.normal_(mean, std, generator=g)
     return t.to(torch.bfloat16)
+
+
+def llama_weights(hidden: int, layers: int, n_q: int, n_kv: int, head_dim: int, ffn: int,
+                  vocab: int, seed: int = 0, device="cuda"):
+    """Random-init weights of a Llama-style stack, drawn on the GPU (see
+    ``device_normal_bf16``): every projection [in, out] ~ N(0, 1/sqrt(in)),
+    the embedding table ~ N(0, 1), RMSNorm gammas ~ N(1, 0.1).  No trained
+    weights exist here; this only gives the stack realistic magnitudes."""
+    def mat(shape, tag):
+        return device_normal_bf16(shape, 0.0, 1.0 / np.sqrt(shape[0]), seed, tag, device)
+
+    def gamma(tag):
+        return device_normal_bf16((hidden,), 1.0, 0.1, seed, tag, device)
+
+    qd, kvd = n_q * head_dim, n_kv * head_dim
+    out = {"embed": device_normal_bf16((vocab, hidden), 0.0, 1.0, seed, "llama.embed", device),
+           "final_norm": gamma("llama.final_norm"),
+           "lm_head": mat((hidden, vocab), "llama.lm_head"),
+           "layers": []}
+    for i in range(layers):
+        t = "llama.%d." % i
+        out["layers"].append({
+            "attn_norm": gamma(t + "attn_norm"), "wq": mat((hidden, qd), t + "wq"),
+            "wk": mat((hidden, kvd), t + "wk"), "wv": mat((hidden, kvd), t + "wv"),
+            "wo": mat((qd, hidden), t + "wo"), "mlp_norm": gamma(t + "mlp_norm"),
+            "w_gate": mat((hidden, ffn), t + "w_gate"), "w_up": mat((hidden, ffn), t + "w_up"),
+            "w_down": mat((ffn, hidden), t + "w_down")})
+    return out
+
+
+def token_ids(n: int, vocab: int, seed: int, tag: str) -> List[int]:
+    """n random token ids, uniform over the vocabulary."""
+    return stream(seed, tag).integers(0, vocab, size=n).tolist()
