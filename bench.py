@@ -313,6 +313,17 @@ def more_sizes(wl):
     out["vendor_gemm_M%d_N%d_K%d" % (M, N, K)] = {
         "torch_matmul_ms": tv, "torch_matmul_TFLOP/s": 2.0 * M * N * K / tv / 1e9,
         "invariant_ms": ti, "invariant_over_vendor": ti / tv}
+    # error-compensated matmul (fp32 operands as hi/lo bf16 pairs, three
+    # products in one fixed order) at the step's shape: cost against bi_matmul
+    a32 = wl.y.float()
+    w3 = bi.matmul_ec_pack_w(wl.w.float())
+    c32 = torch.empty(M, N, dtype=torch.float32, device=dev)
+    ws = torch.empty(M * 3 * K, dtype=torch.bfloat16, device=dev)
+    te = time_call(lambda: bi.matmul_ec(a32, w3, out=c32, workspace=ws))
+    out["matmul_ec_M%d_N%d_K%d" % (M, N, K)] = {
+        "ms": te, "effective_TFLOP/s": 2.0 * M * N * K / te / 1e9,
+        "mfma_TFLOP/s": 3 * 2.0 * M * N * K / te / 1e9, "over_invariant_bf16": te / ti}
+    del a32, w3, c32, ws
     torch.cuda.synchronize()
     return out
 

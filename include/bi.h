@@ -244,6 +244,35 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
  * chosen; a row holding no number gives 0.  out int32 [rows]. */
 int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream);
 
+/* ---- Error-compensated matmul ---------------------------------------------
+ * The HEAL page on gist.science ("Demystifying Numerical Instability in LLM
+ * Inference ... with HEAL", its new-solution section, item 2 on error
+ * compensation) computes a GEMM as a main product in the fast 16-bit format
+ * plus a quick clean-up product that recovers what the main one lost.  The
+ * page gives no formula; the reading here: split each fp32 operand x into
+ * hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in fp32; a non-finite hi
+ * gets lo = 0), and accumulate
+ *     C = hi(A) hi(W) + hi(A) lo(W) + lo(A) hi(W)        (lo lo dropped)
+ * in fp32, in this order, as ONE bi_matmul over K' = 3K of the packed operands
+ *     A3 = [hi(A) | hi(A) | lo(A)]  (bf16 [m, 3k], row by row)
+ *     W3 = [hi(W) ; lo(W) ; hi(W)]  (bf16 [3k, n], stacked along k).
+ * It inherits bi_matmul's invariance (one tile, one k order, no split-K) at
+ * three times its MFMA work; the error is about 2^-16 of sum |a||w| instead
+ * of bf16's 2^-8. */
+
+/* W3 = [hi(w); lo(w); hi(w)]: w fp32 [k, n] -> w3 bf16 [3k, n] (a weight is
+ * packed once). */
+int bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream);
+
+/* Bytes of workspace bi_matmul_ec needs: m * 3k * 2 (the packed A3). */
+size_t bi_matmul_ec_workspace_bytes(int64_t m, int64_t k);
+
+/* c fp32 [m, n] = the error-compensated product of a fp32 [m, k] and the
+ * packed w3 bf16 [3k, n]; k % 64 == 0, n % 8 == 0, 3k <= 2^22.  workspace:
+ * device, >= bi_matmul_ec_workspace_bytes(m, k) bytes, receives A3. */
+int bi_matmul_ec(const float* a, const void* w3, float* c, int64_t m, int64_t n, int64_t k,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ __all__ = [
     "BIError", "lib_path", "load", "abi_version", "rmsnorm", "matmul", "attn_workspace_bytes",
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
-    "embed", "rope", "swiglu", "add", "argmax",
+    "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
 ]
 
 SPLIT = 256
@@ -85,6 +85,9 @@ def load():
         "bi_swiglu": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_add": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_argmax": (ctypes.c_int, [P, P, i64, i64, P]),
+        "bi_matmul_ec_pack_w": (ctypes.c_int, [P, P, i64, i64, P]),
+        "bi_matmul_ec_workspace_bytes": (sz, [i64, i64]),
+        "bi_matmul_ec": (ctypes.c_int, [P, P, P, i64, i64, i64, P, sz, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -378,3 +381,39 @@ def argmax(x: torch.Tensor, out: Optional[torch.Tensor] = None):
         _dev(out, "out", torch.int32, (rows,))
     _check("bi_argmax", load().bi_argmax(_ptr(x), _ptr(o), rows, n, _stream()))
     return o
+
+
+# --------------------------------------------------------------------------- error-compensated matmul
+
+def matmul_ec_pack_w(w: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Pack an fp32 weight [k, n] as bf16 [3k, n] = [hi; lo; hi] for ``matmul_ec``."""
+    _dev(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be [k, n]")
+    k, n = w.shape
+    o = torch.empty(3 * k, n, dtype=torch.bfloat16, device=w.device) if out is None else \
+        _dev(out, "out", torch.bfloat16, (3 * k, n))
+    _check("bi_matmul_ec_pack_w", load().bi_matmul_ec_pack_w(_ptr(w), _ptr(o), k, n, _stream()))
+    return o
+
+
+def matmul_ec(a: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """fp32 C = hi(a)hi(w) + hi(a)lo(w) + lo(a)hi(w) for fp32 a [m, k] and a
+    weight packed by ``matmul_ec_pack_w`` (bf16 [3k, n])."""
+    _dev(a, "a", torch.float32)
+    _dev(w3, "w3", torch.bfloat16)
+    if a.dim() != 2 or w3.dim() != 2 or w3.shape[0] != 3 * a.shape[1]:
+        raise ValueError("need a [m, k] and w3 [3k, n]")
+    m, k = a.shape
+    n = w3.shape[1]
+    c = torch.empty(m, n, dtype=torch.float32, device=a.device) if out is None else \
+        _dev(out, "out", torch.float32, (m, n))
+    lib = load()
+    need = lib.bi_matmul_ec_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 2 + 8, dtype=torch.bfloat16, device=a.device)
+    _check("bi_matmul_ec", lib.bi_matmul_ec(_ptr(a), _ptr(w3), _ptr(c), m, n, k, _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream()))
+    return c

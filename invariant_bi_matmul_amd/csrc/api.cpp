@@ -348,6 +348,48 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
   }
 }
 
+// ---- error-compensated matmul ------------------------------------------------
+
+int bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream) {
+  try {
+    if (k < 0 || n < 0) return BI_ERR_INVALID_SHAPE;
+    if (k == 0 || n == 0) return BI_OK;
+    if (w == nullptr || w3 == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(w) || !aligned16(w3)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_ec_pack_w(w, w3, k, n, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+size_t bi_matmul_ec_workspace_bytes(int64_t m, int64_t k) {
+  if (m < 0 || k < 0) return 0;
+  return (size_t)m * (size_t)(3 * k) * 2;
+}
+
+int bi_matmul_ec(const float* a, const void* w3, float* c, int64_t m, int64_t n, int64_t k,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (m < 0 || n < 0 || k < 0) return BI_ERR_INVALID_SHAPE;
+    if (k > ((int64_t)1 << 22) / 3) return BI_ERR_UNSUPPORTED;
+    // the product itself is bi_matmul over K' = 3k with an fp32 C
+    const int st = check_matmul(workspace, w3, c, BI_DTYPE_F32, m, n, 3 * k);
+    if (st < 0) return BI_OK;
+    if (st != BI_OK) return st;
+    if (k > 0 && a == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(a)) return BI_ERR_INVALID_SHAPE;
+    if (workspace_bytes < bi_matmul_ec_workspace_bytes(m, k)) return BI_ERR_WORKSPACE_TOO_SMALL;
+    const hipStream_t s = (hipStream_t)stream;
+    if (k > 0) {
+      const hipError_t e = bi::launch_ec_pack_a(a, workspace, m, k, s);
+      if (e != hipSuccess) return BI_ERR_HIP;
+    }
+    return hip_status(bi::launch_matmul(workspace, w3, c, true, m, n, 3 * k, s));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
 int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream) {
   try {
     if (rows < 0 || n < 0) return BI_ERR_INVALID_SHAPE;

@@ -60,5 +60,7 @@ hipError_t launch_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int
 hipError_t launch_swiglu(const void* gate, const void* up, void* out, int64_t n, hipStream_t st);
 hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStream_t st);
 hipError_t launch_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, hipStream_t st);
+hipError_t launch_ec_pack_a(const float* a, void* a3, int64_t m, int64_t k, hipStream_t st);
+hipError_t launch_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, hipStream_t st);
 
 }  // namespace bi

@@ -1,6 +1,7 @@
 // Element-wise and per-row operations of a Llama-style decoder stack around
 // the three batch-invariant kernels: token embedding gather, rotary position
-// embedding, SwiGLU, residual add and greedy argmax.
+// embedding, SwiGLU, residual add and greedy argmax; and the operand packing
+// of the error-compensated matmul (fp32 -> bf16 hi/lo planes).
 //
 // None of them reduces across rows: every output element depends only on its
 // own row's inputs (and, for the rotary embedding, on its position), through
@@ -132,6 +133,44 @@ __global__ __launch_bounds__(kElemThreads) void argmax_kernel(const float* __res
   }
 }
 
+// Error-compensated operands: x (fp32) -> hi = bf16(x), lo = bf16(x - hi)
+// (x - hi is exact in fp32).  A non-finite hi has lo = 0.
+__device__ __forceinline__ void ec_split(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16(x);
+  const float h = bf16_to_f32((uint16_t)hi);
+  lo = isfinite(h) ? f32_to_bf16(x - h) : 0u;
+}
+// a3 [m, 3k] = [hi(a) | hi(a) | lo(a)] row by row; one thread per element of a.
+__global__ __launch_bounds__(kElemThreads) void ec_pack_a_kernel(const float* __restrict__ a,
+                                                                 uint16_t* __restrict__ a3,
+                                                                 int64_t m, int64_t k) {
+  const int64_t total = m * k;
+  for (int64_t i = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kElemThreads) {
+    const int64_t r = i / k, c = i - r * k;
+    uint32_t hi, lo;
+    ec_split(a[i], hi, lo);
+    uint16_t* row = a3 + r * 3 * k;
+    row[c] = (uint16_t)hi;
+    row[k + c] = (uint16_t)hi;
+    row[2 * k + c] = (uint16_t)lo;
+  }
+}
+// w3 [3k, n] = [hi(w); lo(w); hi(w)] stacked along k.
+__global__ __launch_bounds__(kElemThreads) void ec_pack_w_kernel(const float* __restrict__ w,
+                                                                 uint16_t* __restrict__ w3,
+                                                                 int64_t k, int64_t n) {
+  const int64_t total = k * n;
+  for (int64_t i = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kElemThreads) {
+    uint32_t hi, lo;
+    ec_split(w[i], hi, lo);
+    w3[i] = (uint16_t)hi;
+    w3[total + i] = (uint16_t)lo;
+    w3[2 * total + i] = (uint16_t)hi;
+  }
+}
+
 unsigned elem_grid(int64_t vecs) {
   int64_t g = (vecs + kElemThreads - 1) / kElemThreads;
   if (g > 65536) g = 65536;
@@ -166,6 +205,18 @@ hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStr
   const int64_t vecs = n / 8;
   hipLaunchKernelGGL(add_kernel, dim3(elem_grid(vecs)), dim3(kElemThreads), 0, st,
                      (const u32x4*)a, (const u32x4*)b, (u32x4*)out, vecs);
+  return hipGetLastError();
+}
+
+hipError_t launch_ec_pack_a(const float* a, void* a3, int64_t m, int64_t k, hipStream_t st) {
+  hipLaunchKernelGGL(ec_pack_a_kernel, dim3(elem_grid(m * k)), dim3(kElemThreads), 0, st, a,
+                     (uint16_t*)a3, m, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(ec_pack_w_kernel, dim3(elem_grid(k * n)), dim3(kElemThreads), 0, st, w,
+                     (uint16_t*)w3, k, n);
   return hipGetLastError();
 }
 
