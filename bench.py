@@ -313,6 +313,33 @@ def more_sizes(wl):
     out["vendor_gemm_M%d_N%d_K%d" % (M, N, K)] = {
         "torch_matmul_ms": tv, "torch_matmul_TFLOP/s": 2.0 * M * N * K / tv / 1e9,
         "invariant_ms": ti, "invariant_over_vendor": ti / tv}
+    # the int16 KV cache (codes + per-(token, kv head) factors) on the step's
+    # attention workloads: the same pages and block tables, random codes
+    shape = (wl.num_pages, NKV, 16, D)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    kc16 = torch.randint(-32767, 32768, shape, dtype=torch.int16, device=dev, generator=g)
+    vc16 = torch.randint(-32767, 32768, shape, dtype=torch.int16, device=dev, generator=g)
+    kf = torch.rand(shape[:3], dtype=torch.float32, device=dev, generator=g) * 1e-4
+    vf = torch.rand(shape[:3], dtype=torch.float32, device=dev, generator=g) * 1e-4
+    od = torch.empty_like(wl.out_dec)
+    op = torch.empty_like(wl.out_pre)
+    td = time_call(lambda: bi.attn_decode_i16(wl.q_dec, wl.k_dec, wl.v_dec, wl.kvl_dec, wl.bt_dec,
+                                              kc16, vc16, kf, vf, wl.scale, out=od))
+    tp = time_call(lambda: bi.attn_prefill_i16(wl.q_pre, wl.k_pre, wl.v_pre, wl.cu_pre,
+                                               wl.kvl_pre, wl.bt_pre, kc16, vc16, kf, vf,
+                                               wl.scale, PREFILL_CHUNK, out=op))
+    w = wl.work()
+    kv_tok = sum(wl.dec_lens)
+    dec_bytes = w["decode"]["bytes"] + kv_tok * NKV * 4 * 2  # + the K and V factors
+    out["int16_kv"] = {
+        "decode_B%d_L%d" % (B_DEC, L_MAX): {"ms": td, "GB/s": dec_bytes / td / 1e6,
+                                            "hbm_frac": dec_bytes / td / 1e6 / HBM_PEAK_GBS,
+                                            "over_bf16_decode": td / time_call(wl.decode)},
+        "prefill_chunk%d_at%d" % (PREFILL_CHUNK, L_MAX): {
+            "ms": tp, "TFLOP/s": w["prefill"]["flops"] / tp / 1e9,
+            "over_bf16_prefill": tp / time_call(wl.prefill)}}
+    del kc16, vc16, kf, vf
     # error-compensated matmul (fp32 operands as hi/lo bf16 pairs, three
     # products in one fixed order) at the step's shape: cost against bi_matmul
     a32 = wl.y.float()

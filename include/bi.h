@@ -244,6 +244,42 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
  * chosen; a row holding no number gives 0.  out int32 [rows]. */
 int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream);
 
+/* ---- Int16 KV cache ----------------------------------------------------------
+ * The HEAL page on gist.science (its new-solution section, item 1) packs the
+ * attention keys and values as INT16 and unpacks them into two 16-bit values
+ * for the matrix units, at no extra memory.  Reading followed here:
+ *   - each (token, kv head) row x (d values) of K or V is stored as
+ *     q = rint(x * (32767 / s)) in int16 (ties to even; fp32 arithmetic),
+ *     s = max |x| over the row, with the dequantisation factor f = s / 32767
+ *     (fp32; 0 for an all-zero row) in a separate array;
+ *   - the caches are int16 [num_pages, n_kv, 16, d] (the bf16 layout, same
+ *     bytes), the factors fp32 [num_pages, n_kv, 16] (16-byte aligned);
+ *   - attention reads q as hi = bf16(q), lo = bf16(q - hi) (both exact, so
+ *     hi + lo = q) and takes two MFMA products for Q K^T and for P V: the
+ *     logit of a key is (q . k_int) * f_k * scale, and the value factor goes
+ *     into the weight before it is rounded to bf16 (the softmax sum keeps
+ *     the unscaled exponentials).
+ * A per-token factor keeps a row's codes independent of what else is in the
+ * cache, so chunking and batching leave them unchanged; splits, their fixed
+ * 256-position boundaries and the fold order are those of bi_attn_prefill.
+ * Inputs must be finite. */
+
+/* As bi_attn_prefill, with the int16 caches and their factor arrays. */
+int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* cu_q, const int32_t* kv_len,
+                        const int32_t* block_table, void* k_cache, void* v_cache, float* k_scale,
+                        float* v_scale, void* out, float* lse, int64_t total_q,
+                        int32_t max_q_per_seq, void* stream);
+
+/* Decode over the int16 cache: one new token per sequence (q, k_new, v_new
+ * [B, ...] as in bi_attn_decode), appended, then attended by the prefill
+ * kernel (one workgroup per sequence and kv head walks the splits in order
+ * and folds them in registers).  No workspace. */
+int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+                       const int32_t* kv_len, const int32_t* block_table, void* k_cache,
+                       void* v_cache, float* k_scale, float* v_scale, void* out, float* lse,
+                       void* stream);
+
 /* ---- Error-compensated matmul ---------------------------------------------
  * The HEAL page on gist.science ("Demystifying Numerical Instability in LLM
  * Inference ... with HEAL", its new-solution section, item 2 on error

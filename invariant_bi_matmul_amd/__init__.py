@@ -21,6 +21,7 @@ __all__ = [
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
+    "attn_prefill_i16", "attn_decode_i16",
 ]
 
 SPLIT = 256
@@ -85,6 +86,9 @@ def load():
         "bi_swiglu": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_add": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_argmax": (ctypes.c_int, [P, P, i64, i64, P]),
+        "bi_attn_prefill_i16": (ctypes.c_int,
+                                [SP, P, P, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
+        "bi_attn_decode_i16": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P]),
         "bi_matmul_ec_pack_w": (ctypes.c_int, [P, P, i64, i64, P]),
         "bi_matmul_ec_workspace_bytes": (sz, [i64, i64]),
         "bi_matmul_ec": (ctypes.c_int, [P, P, P, i64, i64, i64, P, sz, P]),
@@ -417,3 +421,73 @@ def matmul_ec(a: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = N
                                             workspace.numel() * workspace.element_size(),
                                             _stream()))
     return c
+
+
+# --------------------------------------------------------------------------- int16 KV cache
+
+def _i16_cache(k_cache, v_cache, k_scale, v_scale):
+    _dev(k_cache, "k_cache", torch.int16)
+    _dev(v_cache, "v_cache", torch.int16, k_cache.shape)
+    if k_cache.dim() != 4 or k_cache.shape[2] != PAGE:
+        raise ValueError("caches must be int16 [num_pages, n_kv, 16, d]")
+    P, nkv, _, d = k_cache.shape
+    _dev(k_scale, "k_scale", torch.float32, (P, nkv, PAGE))
+    _dev(v_scale, "v_scale", torch.float32, (P, nkv, PAGE))
+    return P, nkv, d
+
+
+def attn_prefill_i16(q, k_new, v_new, cu_q, kv_len, block_table, k_cache, v_cache, k_scale,
+                     v_scale, softmax_scale, max_q_per_seq: int, out=None, lse=None,
+                     with_lse: bool = False):
+    """``attn_prefill`` over the int16 cache: k_new/v_new (bf16) are quantised
+    per (token, kv head) into k_cache/v_cache (int16 [P, n_kv, 16, d]) with
+    their factors in k_scale/v_scale (fp32 [P, n_kv, 16])."""
+    P, nkv, d = _i16_cache(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", torch.bfloat16)
+    T, nq, dq = q.shape
+    if dq != d:
+        raise ValueError("head_dim mismatch")
+    _dev(k_new, "k_new", torch.bfloat16, (T, nkv, d))
+    _dev(v_new, "v_new", torch.bfloat16, (T, nkv, d))
+    _dev(block_table, "block_table", torch.int32)
+    B, maxp = block_table.shape
+    _dev(cu_q, "cu_q", torch.int32, (B + 1,))
+    _dev(kv_len, "kv_len", torch.int32, (B,))
+    o = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16, q.shape)
+    if lse is None and with_lse:
+        lse = torch.empty(T, nq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (T, nq))
+    shape = make_shape(B, nq, nkv, d, maxp, P, softmax_scale)
+    _check("bi_attn_prefill_i16", load().bi_attn_prefill_i16(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_q), _ptr(kv_len),
+        _ptr(block_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(o),
+        _ptr(lse), T, int(max_q_per_seq), _stream()))
+    return (o, lse) if lse is not None else o
+
+
+def attn_decode_i16(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, k_scale, v_scale,
+                    softmax_scale, out=None, lse=None, with_lse: bool = False):
+    """One new token per sequence over the int16 cache; q bf16 [B, n_q, d]."""
+    P, nkv, d = _i16_cache(k_cache, v_cache, k_scale, v_scale)
+    _dev(q, "q", torch.bfloat16)
+    B, nq, dq = q.shape
+    if dq != d:
+        raise ValueError("head_dim mismatch")
+    _dev(k_new, "k_new", torch.bfloat16, (B, nkv, d))
+    _dev(v_new, "v_new", torch.bfloat16, (B, nkv, d))
+    _dev(block_table, "block_table", torch.int32)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table needs one row per sequence")
+    _dev(kv_len, "kv_len", torch.int32, (B,))
+    o = torch.empty_like(q) if out is None else _dev(out, "out", torch.bfloat16, q.shape)
+    if lse is None and with_lse:
+        lse = torch.empty(B, nq, dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, nq))
+    shape = make_shape(B, nq, nkv, d, block_table.shape[1], P, softmax_scale)
+    _check("bi_attn_decode_i16", load().bi_attn_decode_i16(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_len), _ptr(block_table),
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(lse),
+        _stream()))
+    return (o, lse) if lse is not None else o

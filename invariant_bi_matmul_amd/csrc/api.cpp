@@ -348,6 +348,69 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
   }
 }
 
+// ---- int16 KV cache -----------------------------------------------------------
+
+int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* cu_q, const int32_t* kv_len,
+                        const int32_t* block_table, void* k_cache, void* v_cache, float* k_scale,
+                        float* v_scale, void* out, float* lse, int64_t total_q,
+                        int32_t max_q_per_seq, void* stream) {
+  try {
+    const int c = check_attn_shape(s);
+    if (c != BI_OK) return c;
+    if (total_q < 0 || max_q_per_seq < 0) return BI_ERR_INVALID_SHAPE;
+    if (s->num_seqs == 0 || total_q == 0 || max_q_per_seq == 0) return BI_OK;
+    if (max_q_per_seq > total_q) return BI_ERR_INVALID_SHAPE;
+    if (max_q_per_seq > (int64_t)s->max_pages_per_seq * s->page_size) return BI_ERR_INVALID_SHAPE;
+    if (total_q > kMaxGridX || (int64_t)max_q_per_seq * s->num_kv_heads > kMaxGridX)
+      return BI_ERR_UNSUPPORTED;
+    if (!q || !k_new || !v_new || !cu_q || !kv_len || !block_table || !k_cache || !v_cache ||
+        !k_scale || !v_scale || !out)
+      return BI_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(out) ||
+        !aligned4(lse) || !aligned4(cu_q) || !aligned4(kv_len) || !aligned4(block_table))
+      return BI_ERR_INVALID_SHAPE;
+    const bi::AttnDims d = dims_of(s);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bi::launch_kv_append_i16(d, k_new, v_new, cu_q, kv_len, block_table, k_cache,
+                                            v_cache, k_scale, v_scale, max_q_per_seq, st);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    return hip_status(bi::launch_attn_prefill(d, q, cu_q, kv_len, block_table, k_cache, v_cache,
+                                              out, lse, max_q_per_seq, st, k_scale, v_scale));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+                       const int32_t* kv_len, const int32_t* block_table, void* k_cache,
+                       void* v_cache, float* k_scale, float* v_scale, void* out, float* lse,
+                       void* stream) {
+  try {
+    const int c = check_attn_shape(s);
+    if (c != BI_OK) return c;
+    if (s->num_seqs == 0) return BI_OK;
+    if ((int64_t)s->num_seqs * s->num_kv_heads > kMaxGridX) return BI_ERR_UNSUPPORTED;
+    if (!q || !k_new || !v_new || !kv_len || !block_table || !k_cache || !v_cache || !k_scale ||
+        !v_scale || !out)
+      return BI_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(out) ||
+        !aligned4(lse) || !aligned4(kv_len) || !aligned4(block_table))
+      return BI_ERR_INVALID_SHAPE;
+    const bi::AttnDims d = dims_of(s);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bi::launch_kv_append_i16(d, k_new, v_new, nullptr, kv_len, block_table,
+                                            k_cache, v_cache, k_scale, v_scale, 1, st);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    return hip_status(bi::launch_attn_prefill(d, q, nullptr, kv_len, block_table, k_cache,
+                                              v_cache, out, lse, 1, st, k_scale, v_scale));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
 // ---- error-compensated matmul ------------------------------------------------
 
 int bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream) {

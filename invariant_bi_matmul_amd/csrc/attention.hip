@@ -234,6 +234,28 @@ struct StagedSrc {
   }
 };
 
+// The same over the int16 cache: the operands are int16, and the split's 256
+// key and value dequantisation factors sit in LDS (kscl, vscl).  kscale<C> /
+// vscale(C) give this lane's keys 32C + 8q .. +7.
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+template <int D>
+struct StagedSrc16 : StagedSrc<D> {
+  static constexpr bool Q16 = true;
+  uint32_t kscl, vscl;
+  __device__ __forceinline__ void factors(uint32_t base, int C, float (&f)[8]) const {
+    const int q = (threadIdx.x & (kWave - 1)) >> 4;
+    const uint32_t a = base + (uint32_t)(32 * C + 8 * q) * 4;
+    const f32x4 x = *(lds_f32x4*)(uintptr_t)a, y = *(lds_f32x4*)(uintptr_t)(a + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = x[j];
+      f[4 + j] = y[j];
+    }
+  }
+  __device__ __forceinline__ void kscale(int C, float (&f)[8]) const { factors(kscl, C, f); }
+  __device__ __forceinline__ void vscale(int C, float (&f)[8]) const { factors(vscl, C, f); }
+};
+
 // A split streamed chunk by chunk through a wave-private ring of RING LDS
 // slots (decode): the 16 chunk loads (K0..K7 then V0..V7) run RING-1 ahead.
 constexpr int kRing = 5;  // 5 slots x 8 KiB x 4 waves = the 160 KiB of a CU at d=128
@@ -321,6 +343,22 @@ struct RingSrc {
   }
 };
 
+// Eight int16 values (a K or V operand of the int16 cache) as two exact bf16
+// operands: hi = bf16(v) and lo = bf16(v - hi); v has at most 16 significant
+// bits, so hi + lo == v exactly and an MFMA with hi then lo adds v * b.
+__device__ __forceinline__ void unpack_i16x8(u32x4 raw, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = (float)(int16_t)(raw[j] & 0xffffu);
+    const float b = (float)(int16_t)(raw[j] >> 16);
+    h[j] = pack_bf16x2(a, b);
+    l[j] = pack_bf16x2(a - bf16_lo(h[j]), b - bf16_hi(h[j]));
+  }
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
 // ---- the split partial, in two phases -----------------------------------------
 // Lane l (r = l%16, q = l/16) owns column r of each of its NB blocks; block b's
 // query sits at position pcol[b]; key j is valid iff j <= pcol[b] and
@@ -334,6 +372,12 @@ struct RingSrc {
 // else would hide it).
 constexpr int kOperandsAhead = 4;
 
+// Whether an operand source reads the int16 cache (Src::Q16, default false).
+template <class S, class = void>
+struct SrcQ16 : std::false_type {};
+template <class S>
+struct SrcQ16<S, std::void_t<decltype(S::Q16)>> : std::integral_constant<bool, S::Q16> {};
+
 template <int D, int NB, class Src>
 __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, int pmin,
                                          const bf16x8 (&qf)[NB][KV<D>::DS], const int (&pcol)[NB],
@@ -343,6 +387,7 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
   constexpr int OPC = 2 * DS;      // K operands per 32-key chunk: (half h, d-step t)
   constexpr int NOP = 8 * OPC;
   constexpr int PD = kOperandsAhead;
+  constexpr bool Q16 = SrcQ16<Src>::value;
   const int q = (threadIdx.x & (kWave - 1)) >> 4;
   float z[NB][8][8];
   u32x4 buf[PD];
@@ -363,12 +408,30 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = f32x4{};
     }
-    const bf16x8 a = as_bf16x8(buf[o % PD]);
+    const u32x4 raw = buf[o % PD];
     if constexpr (o + PD < NOP) read(std::integral_constant<int, o + PD>{});
+    if constexpr (Q16) {
+      bf16x8 hi, lo;
+      unpack_i16x8(raw, hi, lo);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b][h] = mfma16(a, qf[b][t], acc[b][h]);
+      for (int b = 0; b < NB; ++b) {
+        acc[b][h] = mfma16(hi, qf[b][t], acc[b][h]);
+        acc[b][h] = mfma16(lo, qf[b][t], acc[b][h]);
+      }
+    } else {
+      const bf16x8 a = as_bf16x8(raw);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b][h] = mfma16(a, qf[b][t], acc[b][h]);
+    }
     if constexpr (o % OPC == OPC - 1) {
-      // raw dot products; -inf marks an invalid key
+      // dot products (int16 cache: times the key's factor); -inf marks an
+      // invalid key
+      float fk[8];
+      if constexpr (Q16) src.kscale(c, fk);
+      auto dot = [&](int b, int hh, int i) __attribute__((always_inline)) {
+        if constexpr (Q16) return acc[b][hh][i] * fk[4 * hh + i];
+        else return acc[b][hh][i];
+      };
       const int last = key0 + 32 * c + 31;
       if (last <= pmin && last < key_end) {
 #pragma unroll
@@ -376,7 +439,7 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[b][c][4 * hh + i] = acc[b][hh][i];
+            for (int i = 0; i < 4; ++i) z[b][c][4 * hh + i] = dot(b, hh, i);
       } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -386,7 +449,7 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
             for (int i = 0; i < 4; ++i) {
               const int key = key0 + 32 * c + 8 * q + 4 * hh + i;
               const bool ok = key <= pcol[b] && key < key_end;
-              z[b][c][4 * hh + i] = ok ? acc[b][hh][i] : -INFINITY;
+              z[b][c][4 * hh + i] = ok ? dot(b, hh, i) : -INFINITY;
             }
       }
     }
@@ -416,6 +479,14 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
       for (int j = 0; j < 8; ++j) {
         e[j] = fast_exp2(fmaf(z[b][c][j], c2, -ms));
         ll = ll + e[j];
+      }
+      if constexpr (Q16) {
+        // the value factor goes into the weight (the sum l keeps e itself); an
+        // invalid key has e = 0 and its factor may be anything
+        float fv[8];
+        src.vscale(c, fv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = e[j] != 0.0f ? e[j] * fv[j] : 0.0f;
       }
       p[b][c] = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
                       pack_bf16x2(e[6], e[7])};
@@ -452,8 +523,18 @@ __device__ __forceinline__ void split_pv(const Src& src, const u32x4 (&p)[NB][8]
     constexpr int c = op / DB, i = op % DB;
     const bf16x8 va = buf[op % PD];
     if constexpr (op + PD < NOP) read(std::integral_constant<int, op + PD>{});
+    if constexpr (SrcQ16<Src>::value) {
+      bf16x8 hi, lo;
+      unpack_i16x8(__builtin_bit_cast(u32x4, va), hi, lo);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) o[b][i] = mfma16(va, as_bf16x8(p[b][c]), o[b][i]);
+      for (int b = 0; b < NB; ++b) {
+        o[b][i] = mfma16(hi, as_bf16x8(p[b][c]), o[b][i]);
+        o[b][i] = mfma16(lo, as_bf16x8(p[b][c]), o[b][i]);
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) o[b][i] = mfma16(va, as_bf16x8(p[b][c]), o[b][i]);
+    }
   });
 }
 
@@ -518,6 +599,57 @@ __global__ __launch_bounds__(128) void kv_append_kernel(const uint16_t* __restri
     const int64_t dst = ((((int64_t)page * nkv + g) << 4) + slot) * D + e;
     *(u32x4*)(kc + dst) = *(const u32x4*)(k_new + src);
     *(u32x4*)(vc + dst) = *(const u32x4*)(v_new + src);
+  }
+}
+
+// Int16 cache: each (token, kv head) row x of K or V is stored as
+// q = rint(x * (32767 / s)) (int16, ties to even) with s = max |x| over the
+// row, and its dequantisation factor f = s / 32767 (fp32; 0 for an all-zero
+// row) in a [pages, n_kv, 16] array.  One wave per (token, kv head): the max
+// is exact and order-free.
+template <int D>
+__global__ __launch_bounds__(64) void kv_append_i16_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ kv_len,
+    const int32_t* __restrict__ bt, int16_t* __restrict__ kc, int16_t* __restrict__ vc,
+    float* __restrict__ ks, float* __restrict__ vs, int nkv, int max_pages) {
+  constexpr int PER = D / kWave;  // elements per lane
+  const int b = blockIdx.y;
+  const int i = blockIdx.x / nkv, g = blockIdx.x % nkv;
+  int tok0 = b, nb = 1;
+  if (cu_q != nullptr) {
+    tok0 = cu_q[b];
+    nb = cu_q[b + 1] - tok0;
+  }
+  if (i >= nb) return;
+  const int lane = threadIdx.x;
+  const int pos = kv_len[b] - nb + i;
+  const int64_t tok = tok0 + i;
+  const int page = bt[(int64_t)b * max_pages + (pos >> 4)];
+  const int slot = pos & 15;
+  const int64_t src = (tok * nkv + g) * D + lane * PER;
+  const int64_t row = (((int64_t)page * nkv + g) << 4) + slot;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint16_t* x = (kv ? v_new : k_new) + src;
+    float v[PER];
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      v[e] = bf16_to_f32(x[e]);
+      s = fmaxf(s, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) s = fmaxf(s, __shfl_xor(s, d));
+    const float inv = 32767.0f / s;
+    int16_t* dst = (kv ? vc : kc) + row * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      float qv = s > 0.0f ? rintf(v[e] * inv) : 0.0f;
+      qv = fminf(fmaxf(qv, -32767.0f), 32767.0f);
+      dst[e] = (int16_t)qv;
+    }
+    if (lane == 0) (kv ? vs : ks)[row] = s / 32767.0f;
   }
 }
 
@@ -869,13 +1001,43 @@ struct StageLaneOffs {
   }
 };
 
+// The int16 cache's factors of a split's 256 keys (one 1 KiB load by one
+// wave: lane l brings keys key0 + 4l .. +3, in page (key0 + 4l)/16, read from
+// the block table; past the last position the page is the last one's, and
+// those keys' factors are never used).
+__device__ __forceinline__ void stage_factors(const float* fpool, const int32_t* bt_row, int key0,
+                                              int last, int nkv, int g, uint8_t* lds) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int page = bt_row[min(key0 + 4 * lane, last) >> 4];
+  lds_dma16(fpool + (((int64_t)page * nkv + g) << 4) + 4 * (lane & 3),
+            (uint32_t)(uintptr_t)lds);
+}
+
+// With an int16 cache the K stage also brings the split's key factors (wave
+// 0) and value factors (wave 1): both are read while the logits and weights
+// are formed, before the value rows are waited for.
+struct SplitFactors {
+  const float* kf = nullptr;
+  const float* vf = nullptr;
+  uint8_t* klds = nullptr;
+  uint8_t* vlds = nullptr;
+  const int32_t* bt_row = nullptr;
+};
+
 template <int D, bool IS_K>
 __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPages& sp, int nkv,
                                             int g, int key0, int last, uint8_t* lds,
-                                            const StageLaneOffs<D>& offs) {
+                                            const StageLaneOffs<D>& offs,
+                                            const SplitFactors& fac = SplitFactors{}) {
   constexpr int KPI = kWave / KV<D>::CPR;       // keys per 1 KiB load
   constexpr int NLOAD = 256 / KPI / 4;          // loads per thread (4 waves)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (IS_K && fac.kf != nullptr) {
+    // before the row loads: the block-table read is waited for here, with no
+    // direct load of this stage in flight yet
+    if (wave == 0) stage_factors(fac.kf, fac.bt_row, key0, last, nkv, g, fac.klds);
+    if (wave == 1) stage_factors(fac.vf, fac.bt_row, key0, last, nkv, g, fac.vlds);
+  }
   const bool hi = ((wave * KPI) >> 4) != 0;     // the wave's keys start in the next page
   const uint32_t base = (uint32_t)(uintptr_t)lds;
   if (key0 + kSplit - 1 <= last) {
@@ -902,15 +1064,19 @@ __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPag
   }
 }
 
-template <int D>
+// Q16: the cache holds int16 rows with per-(page, kv head, slot) factors
+// kf / vf (nullptr otherwise).  cu_q == nullptr means one token per sequence.
+template <int D, bool Q16>
 __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ bt,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int nq, int nkv, int max_pages, float c2) {
+    float* __restrict__ lse, int nq, int nkv, int max_pages, float c2,
+    const float* __restrict__ kf, const float* __restrict__ vf) {
   constexpr int NB = kPrefillNB, DB = KV<D>::DB;
   __shared__ __attribute__((aligned(1024))) uint8_t klds[256 * KV<D>::ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t vlds[256 * KV<D>::ROWB];
+  __shared__ __attribute__((aligned(1024))) uint8_t flds[Q16 ? 2 * 1024 : 16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.z, g = blockIdx.y;
@@ -918,8 +1084,8 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   const int group = nq / nkv;
   const int ppb = 16 / group;  // positions per block
   const int per_wg = 4 * NB * ppb;
-  const int tok0 = cu_q[b];
-  const int nb = cu_q[b + 1] - tok0;
+  const int tok0 = cu_q != nullptr ? cu_q[b] : b;
+  const int nb = cu_q != nullptr ? cu_q[b + 1] - tok0 : 1;
   if (tile * per_wg >= nb) return;  // whole workgroup: no barrier reached
   const int L = kv_len[b];
   const int start = L - nb;
@@ -943,8 +1109,15 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   const int pmin = start + tile * per_wg + wave * NB * ppb;
   const int nsplit = pmax / kSplit + 1;
   const int32_t* bt_row = bt + (int64_t)b * max_pages;
-  StagedSrc<D> src;
+  using Src = std::conditional_t<Q16, StagedSrc16<D>, StagedSrc<D>>;
+  Src src;
   src.ol.init((uint32_t)(uintptr_t)klds, (uint32_t)(uintptr_t)vlds);
+  SplitFactors fac;
+  if constexpr (Q16) {
+    fac = SplitFactors{kf, vf, flds, flds + 1024, bt_row};
+    src.kscl = (uint32_t)(uintptr_t)fac.klds;
+    src.vscl = (uint32_t)(uintptr_t)fac.vlds;
+  }
 
   float M[NB], Lsum[NB];
   f32x4 O[NB][DB];
@@ -959,7 +1132,7 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   pages.load(bt_row, 0, L - 1);
   StageLaneOffs<D> soffs;
   soffs.init(wave);
-  stage_split<D, true>(kc, pages, nkv, g, 0, L - 1, klds, soffs);
+  stage_split<D, true>(kc, pages, nkv, g, 0, L - 1, klds, soffs, fac);
   for (int s = 0; s < nsplit; ++s) {
     const int key0 = s * kSplit;
     wait_vmcnt_le<0>();
@@ -974,7 +1147,7 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     __syncthreads();  // V(s) in LDS; every wave is done reading K(s)
     if (s + 1 < nsplit) {
       pages = next;
-      stage_split<D, true>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs);
+      stage_split<D, true>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs, fac);
     }
     f32x4 os[NB][DB];
     split_pv<D, NB>(src, p, os);
@@ -1096,19 +1269,45 @@ hipError_t launch_kv_append(const AttnDims& s, const void* k_new, const void* v_
 hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* cu_q,
                                const int32_t* kv_len, const int32_t* bt, const void* kc,
                                const void* vc, void* out, float* lse, int max_q_per_seq,
-                               hipStream_t st) {
+                               hipStream_t st, const float* kf, const float* vf) {
   const int per_wg = 4 * kPrefillNB * (16 / (s.nq / s.nkv));
   const dim3 grid((unsigned)((max_q_per_seq + per_wg - 1) / per_wg), (unsigned)s.nkv,
                   (unsigned)s.B);
   const float c2 = base2_scale(s.scale);
+  const bool q16 = kf != nullptr;
+#define BI_PREFILL(DD, QQ)                                                                     \
+  hipLaunchKernelGGL((bi_attn_prefill_kernel<DD, QQ>), grid, dim3(256), 0, st,                 \
+                     (const uint16_t*)q, cu_q, kv_len, bt, (const uint16_t*)kc,                \
+                     (const uint16_t*)vc, (uint16_t*)out, lse, s.nq, s.nkv, s.max_pages, c2, kf, \
+                     vf)
+  if (s.d == 128) {
+    if (q16)
+      BI_PREFILL(128, true);
+    else
+      BI_PREFILL(128, false);
+  } else {
+    if (q16)
+      BI_PREFILL(64, true);
+    else
+      BI_PREFILL(64, false);
+  }
+#undef BI_PREFILL
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_i16(const AttnDims& s, const void* k_new, const void* v_new,
+                                const int32_t* cu_q, const int32_t* kv_len, const int32_t* bt,
+                                void* kc, void* vc, float* kf, float* vf, int max_q_per_seq,
+                                hipStream_t st) {
+  const dim3 grid((unsigned)((int64_t)max_q_per_seq * s.nkv), (unsigned)s.B);
   if (s.d == 128)
-    hipLaunchKernelGGL(bi_attn_prefill_kernel<128>, grid, dim3(256), 0, st, (const uint16_t*)q,
-                       cu_q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
-                       (uint16_t*)out, lse, s.nq, s.nkv, s.max_pages, c2);
+    hipLaunchKernelGGL(kv_append_i16_kernel<128>, grid, dim3(64), 0, st, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, cu_q, kv_len, bt, (int16_t*)kc, (int16_t*)vc, kf,
+                       vf, s.nkv, s.max_pages);
   else
-    hipLaunchKernelGGL(bi_attn_prefill_kernel<64>, grid, dim3(256), 0, st, (const uint16_t*)q,
-                       cu_q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
-                       (uint16_t*)out, lse, s.nq, s.nkv, s.max_pages, c2);
+    hipLaunchKernelGGL(kv_append_i16_kernel<64>, grid, dim3(64), 0, st, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, cu_q, kv_len, bt, (int16_t*)kc, (int16_t*)vc, kf,
+                       vf, s.nkv, s.max_pages);
   return hipGetLastError();
 }
 

@@ -39,10 +39,17 @@ struct AttnDims {
 hipError_t launch_kv_append(const AttnDims& s, const void* k_new, const void* v_new,
                             const int32_t* cu_q, const int32_t* kv_len, const int32_t* bt,
                             void* kc, void* vc, int max_q_per_seq, hipStream_t st);
+// kf/vf non-null: the caches hold int16 rows with per-(page, kv head, slot)
+// fp32 dequantisation factors; cu_q == nullptr: one token per sequence.
 hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* cu_q,
                                const int32_t* kv_len, const int32_t* bt, const void* kc,
                                const void* vc, void* out, float* lse, int max_q_per_seq,
-                               hipStream_t st);
+                               hipStream_t st, const float* kf = nullptr,
+                               const float* vf = nullptr);
+hipError_t launch_kv_append_i16(const AttnDims& s, const void* k_new, const void* v_new,
+                                const int32_t* cu_q, const int32_t* kv_len, const int32_t* bt,
+                                void* kc, void* vc, float* kf, float* vf, int max_q_per_seq,
+                                hipStream_t st);
 hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
                               const int32_t* bt, const void* kc, const void* vc, void* out,
                               float* lse, int max_splits, float* ws, hipStream_t st);
