@@ -355,7 +355,291 @@ def more_sizes(wl):
     return out
 
 
-def cpu_baseline(wl, target_s=10.0):
+def time_rotating(fns, reps):
+    """Average ms per call over `reps` calls cycling through `fns` (each one a
+    different buffer set, so the working set stays out of the caches)."""
+    import torch
+    for f in fns:
+        f()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+ROTATE_BYTES = 512 << 20   # twice the 256 MiB MALL
+CUS = 256
+MFMA_FLOPS_PER_CU_CLK = 4096   # dense bf16: 2.5 PFLOP/s = 256 CUs x 4096 x 2.4 GHz
+
+
+def ceilings():
+    """Measured ceilings beside the datasheet peaks: a 4 GiB device copy (read +
+    write), a 4 GiB read-only sweep (bix_read_stream), and an MFMA-only
+    register loop (bix_mfma_loop), whose rate over 4096 flop per CU per clock
+    gives the clock the chip holds under matrix load."""
+    import torch
+    import invariant_bi_matmul_amd as bi
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ms = time_call(lambda: dst.copy_(src), reps=5, warmup=1)
+    out = {"copy_4GiB": {"GB/s": 2 * 4 * n / ms / 1e6, "ms": ms,
+                         "kernel": "torch copy_ (read 4 GiB + write 4 GiB)"}}
+    del dst
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    best = None
+    for wg in (1024, 2048, 4096, 8192):
+        ms = time_call(lambda: bi.bix_read_stream(src, wg, sink), reps=5, warmup=1)
+        gbs = 4 * n / ms / 1e6
+        if best is None or gbs > best["GB/s"]:
+            best = {"GB/s": gbs, "ms": ms, "workgroups": wg}
+    out["read_4GiB"] = best
+    del src
+    fsink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    best = None
+    iters = 20000
+    for wg in (CUS * 4, CUS * 8):
+        fl = 4.0 * 4 * 32768 * iters * wg
+        ms = time_call(lambda: bi.bix_mfma_loop(iters, wg, fsink), reps=5, warmup=1)
+        tf = fl / ms / 1e9
+        if best is None or tf > best["TFLOP/s"]:
+            best = {"TFLOP/s": tf, "ms": ms, "workgroups": wg, "waves_per_simd": wg // CUS,
+                    "implied_clock_GHz": tf * 1e12 / (CUS * MFMA_FLOPS_PER_CU_CLK) / 1e9}
+    out["mfma_bf16_loop"] = best
+    torch.cuda.synchronize()
+    return out
+
+
+def _grid_fill(tiles):
+    """Fraction of CU-slots busy when `tiles` workgroups (one per CU at a
+    time) run in ceil(tiles / 256) rounds."""
+    rounds = -(-tiles // CUS)
+    return tiles / (rounds * CUS)
+
+
+def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
+    """The configurations' sizes, each timed over rotating buffer sets of at
+    least 512 MiB so that every launch reads from HBM, not the MALL.
+
+    matmul: M in {1,2,7,16,64,256,512,2048}, N in {4096, 14336}, K=4096:
+    TFLOP/s, fraction of the bf16 peak, of the roofline min(peak, AI x 8 TB/s)
+    and the grid-fill ceiling of the fixed 256x128 tile; beside it the vendor
+    GEMM (torch.matmul, not batch-invariant) on the same buffers.  RMSNorm: R in
+    {1..16384 powers of two, 3, 7, 1000, 16383}, H in {4096, 8192}.  Decode:
+    L in {512, 4096, 32768} x B in {1..64}, lengths ragged U{L/2..L} with one
+    probe at L, shuffled 16-token pages.  Prefill: one sequence of L tokens,
+    one-shot against 512-token chunks (and whether they agree bit for bit)."""
+    import torch
+    bi, synth, dev, np = wl.bi, wl.synth, wl.dev, wl.np
+    out = {"matmul": {}, "rmsnorm": {}, "decode": {}, "prefill": {}}
+    a_full = wl.y
+    bi.rmsnorm(wl.x, wl.g, wl.eps, out=wl.y)
+    for n in (4096, 14336) if "matmul" in parts else ():
+        log("sweep: matmul N=%d" % n)
+        wbytes = K * n * 2
+        sets = max(1, -(-ROTATE_BYTES // wbytes))
+        ws = [synth.device_normal_bf16((K, n), 0.0, 0.125, 0, "sweep.w%d.%d" % (n, i), dev)
+              for i in range(sets)]
+        for m in (1, 2, 7, 16, 64, 256, 512, 2048):
+            a = a_full[:m].contiguous()
+            cs = [torch.empty(m, n, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+            fns = [(lambda w=w, c=c: bi.matmul(a, w, out=c)) for w, c in zip(ws, cs)]
+            ms = time_rotating(fns, max(40, 2 * sets))
+            vfns = [(lambda w=w, c=c: torch.matmul(a, w, out=c)) for w, c in zip(ws, cs)]
+            vms = time_rotating(vfns, max(40, 2 * sets))
+            flops = 2.0 * m * n * K
+            by = 2.0 * (m * K + K * n + m * n)
+            tf = flops / ms / 1e9
+            roof = min(MFMA_BF16_PEAK, flops / by * HBM_PEAK_GBS / 1e3)
+            tiles = -(-m // 256) * (n // 128)
+            out["matmul"]["M%d_N%d" % (m, n)] = {
+                "ms": ms, "TFLOP/s": tf, "mfma_frac": tf / MFMA_BF16_PEAK,
+                "roofline_TFLOP/s": roof, "roofline_frac": tf / roof,
+                "GB/s": by / ms / 1e6, "tiles": tiles, "grid_fill_ceiling": _grid_fill(tiles),
+                "vendor_ms": vms, "invariant_over_vendor": ms / vms}
+            del cs
+        del ws
+    for h in (4096, 8192) if "rmsnorm" in parts else ():
+        log("sweep: rmsnorm H=%d" % h)
+        rows_big = ROTATE_BYTES // (2 * h)
+        xb = synth.device_normal_bf16((rows_big, h), 0.0, 1.0, 0, "sweep.rms%d" % h, dev)
+        yb = torch.empty_like(xb)
+        g = synth.device_normal_bf16((h,), 1.0, 0.1, 0, "sweep.rmsg%d" % h, dev)
+        for r in sorted({1 << i for i in range(15)} | {3, 7, 1000, 16383}):
+            sets = max(1, min(256, rows_big // r))
+            fns = [(lambda i=i: bi.rmsnorm(xb[i * r:(i + 1) * r], g, wl.eps,
+                                           out=yb[i * r:(i + 1) * r])) for i in range(sets)]
+            ms = time_rotating(fns, max(20, sets))
+            by = 4.0 * h * r + 2 * h
+            out["rmsnorm"]["R%d_H%d" % (r, h)] = {"ms": ms, "GB/s": by / ms / 1e6,
+                                                  "hbm_frac": by / ms / 1e6 / HBM_PEAK_GBS}
+        del xb, yb
+    for L in (512, 4096, 32768) if "decode" in parts else ():
+        log("sweep: decode L=%d" % L)
+        for bsz in (1, 2, 4, 8, 16, 32, 64):
+            lens, _ = synth.ragged_lengths(bsz, L, seed=0)
+            pages = [(l + 15) // 16 for l in lens]
+            set_bytes = sum(lens) * NKV * D * 2 * 2
+            sets = max(1, min(64, -(-ROTATE_BYTES // set_bytes)))
+            num = sets * sum(pages) + 3
+            perm = synth.stream(0, "sweep.dec.%d.%d" % (bsz, L)).permutation(num).astype(np.int32)
+            kc = synth.device_normal_bf16((num, NKV, 16, D), 0.0, 1.0, 0, "sweep.dk", dev)
+            vc = synth.device_normal_bf16((num, NKV, 16, D), 0.0, 1.0, 0, "sweep.dv", dev)
+            bts = []
+            cur = 0
+            for _ in range(sets):
+                bt = np.full((bsz, max(pages)), -1, dtype=np.int32)
+                for b, p in enumerate(pages):
+                    bt[b, :p] = perm[cur:cur + p]
+                    cur += p
+                bts.append(torch.from_numpy(bt).to(dev))
+            q = synth.device_normal_bf16((bsz, NQ, D), 0.0, 1.0, 0, "sweep.dq", dev)
+            kn = synth.device_normal_bf16((bsz, NKV, D), 0.0, 1.0, 0, "sweep.dkn", dev)
+            vn = synth.device_normal_bf16((bsz, NKV, D), 0.0, 1.0, 0, "sweep.dvn", dev)
+            kvl = torch.tensor(lens, dtype=torch.int32, device=dev)
+            o = torch.empty(bsz, NQ, D, dtype=torch.bfloat16, device=dev)
+            ash = bi.make_shape(bsz, NQ, NKV, D, max(pages), num, wl.scale)
+            wsp = torch.empty(bi.attn_workspace_bytes(ash, bsz, L) // 4 + 4, dtype=torch.float32,
+                              device=dev)
+            fns = [(lambda bt=bt: bi.attn_decode(q, kn, vn, kvl, bt, kc, vc, wl.scale, L,
+                                                 workspace=wsp, out=o)) for bt in bts]
+            ms = time_rotating(fns, max(20, sets))
+            by = set_bytes + bsz * NQ * D * 2 * 2 + bsz * NKV * D * 2 * 2
+            out["decode"]["B%d_L%d" % (bsz, L)] = {"ms": ms, "GB/s": by / ms / 1e6,
+                                                   "hbm_frac": by / ms / 1e6 / HBM_PEAK_GBS,
+                                                   "kv_tokens": sum(lens)}
+            del kc, vc, bts
+    for L in (512, 4096, 32768) if "prefill" in parts else ():
+        log("sweep: prefill L=%d" % L)
+        kc, vc, bt = _paged(wl, [L], "sweep.pre%d" % L)
+        q = synth.device_normal_bf16((L, NQ, D), 0.0, 1.0, 0, "sweep.pq%d" % L, dev)
+        kn = synth.device_normal_bf16((L, NKV, D), 0.0, 1.0, 0, "sweep.pk%d" % L, dev)
+        vn = synth.device_normal_bf16((L, NKV, D), 0.0, 1.0, 0, "sweep.pv%d" % L, dev)
+        one = torch.empty_like(q)
+        chk = torch.empty_like(q)
+        cu_one = torch.tensor([0, L], dtype=torch.int32, device=dev)
+        kvl_one = torch.tensor([L], dtype=torch.int32, device=dev)
+        C = PREFILL_CHUNK
+        cu_c = torch.tensor([0, C], dtype=torch.int32, device=dev)
+        kvls = [torch.tensor([s + C], dtype=torch.int32, device=dev) for s in range(0, L, C)]
+
+        def chunked():
+            for i, s in enumerate(range(0, L, C)):
+                bi.attn_prefill(q[s:s + C], kn[s:s + C], vn[s:s + C], cu_c, kvls[i], bt, kc, vc,
+                                wl.scale, C, out=chk[s:s + C])
+
+        reps = 3 if L > 4096 else 10
+        t1 = time_call(lambda: bi.attn_prefill(q, kn, vn, cu_one, kvl_one, bt, kc, vc, wl.scale,
+                                               L, out=one), reps=reps, warmup=1)
+        tc = time_call(chunked, reps=reps, warmup=1)
+        fl = 8192.0 * L * (L + 1)
+        out["prefill"]["L%d" % L] = {
+            "one_shot_ms": t1, "one_shot_TFLOP/s": fl / t1 / 1e9,
+            "one_shot_mfma_frac": fl / t1 / 1e9 / MFMA_BF16_PEAK,
+            "chunked512_ms": tc, "chunked512_TFLOP/s": fl / tc / 1e9,
+            "chunked_bitwise_equal_one_shot": bool(torch.equal(one.view(torch.int16),
+                                                               chk.view(torch.int16)))}
+        del kc, vc, q, kn, vn, one, chk
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _timed(run, units, target_s, max_n=None):
+    """Grow n until run(n) takes a quarter of target_s, then time run(n)
+    scaled to about target_s seconds (n at most max_n).  Returns (n, units(n)
+    per second, seconds)."""
+    cap = (lambda v: v) if max_n is None else (lambda v: min(v, max_n))
+    n = 1
+    while True:
+        t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n == cap(n + 1):
+            break
+        n = cap(n * 8 if dt < 1e-3 else int(n * min(8.0, target_s / 2 / dt)) + 1)
+    n = cap(max(n, int(n * target_s / dt)))
+    t0 = time.perf_counter()
+    run(n)
+    dt = time.perf_counter() - t0
+    return n, units(n) / dt, dt
+
+
+def cpu_oracle(wl, target_s=3.0):
+    """The oracle on the host, on all cores and on one, in the GPU side's
+    units: the matmul (TFLOP/s over rows of A x the full W), RMSNorm (GB/s over
+    rows of x) and decode attention (GB/s over sequences of the decode batch,
+    keys and values gathered from the paged pool)."""
+    import numpy as np
+    import oracle
+    torch = wl.torch
+    oracle.build(force=False)
+    a_bits = wl.y.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    x_rows = np.tile(wl.x_bits, (4, 1))
+    # the decode batch's keys and values, unpaged, and its queries
+    bt = wl.bt_host
+    kc = wl.kc.view(torch.int16).cpu().numpy().view(np.uint16)
+    vc = wl.vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    qd = wl.q_dec.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def unpage(pool, b):
+        L = wl.dec_lens[b]
+        p = bt[b, :(L + 15) // 16]
+        return np.ascontiguousarray(pool[p].transpose(0, 2, 1, 3).reshape(-1, NKV, D)[:L])
+
+    lens = wl.dec_lens
+    k_all = np.concatenate([unpage(kc, b) for b in range(B_DEC)])
+    v_all = np.concatenate([unpage(vc, b) for b in range(B_DEC)])
+    off = np.concatenate([[0], np.cumsum(lens)])
+
+    def decode(n):
+        # the first n sequences of the batch: their keys are a prefix of k_all
+        oracle.attention(qd[:n], k_all[:off[n]], v_all[:off[n]], lens[:n], list(range(n)),
+                         [L - 1 for L in lens[:n]], wl.scale, threads=threads)
+
+    def rmsnorm(n):
+        # n rows, in calls over the 8192 rows at hand
+        for s in range(0, n, x_rows.shape[0]):
+            oracle.rmsnorm(x_rows[:min(n - s, x_rows.shape[0])], wl.g_bits, wl.eps,
+                           threads=threads)
+
+    def decode_seqs(n):
+        # n sequences, in passes over the 64 of the decode batch
+        for s in range(0, n, B_DEC):
+            decode(min(n - s, B_DEC))
+
+    kv_bytes = lambda n: sum(wl.dec_lens[i % B_DEC] for i in range(n)) * NKV * D * 4 / 1e9
+    out = {"cores": oracle.default_threads(), "model": _cpu_model(), "kind": "oracle"}
+    for label, threads in (("all_cores", oracle.default_threads()), ("one_core", 1)):
+        r = {}
+        n, v, dt = _timed(lambda n: oracle.matmul(a_bits, wl.w_bits, rows=range(n),
+                                                  threads=threads),
+                          lambda n: 2.0 * n * N * K / 1e12, target_s, M)
+        r["matmul_TFLOP/s"] = {"value": v, "rows": n, "s": dt}
+        n, v, dt = _timed(rmsnorm, lambda n: 4.0 * H * n / 1e9, target_s)
+        r["rmsnorm_GB/s"] = {"value": v, "rows": n, "s": dt}
+        n, v, dt = _timed(decode_seqs, kv_bytes, target_s)
+        r["decode_GB/s"] = {"value": v, "sequences": n, "s": dt}
+        out[label] = r
+    return out
+
+
+def cpu_baseline(wl, target_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the step's matmul:
     rows of A (the RMSNorm output) times the full W, timed on this host."""
     import numpy as np
@@ -363,17 +647,10 @@ def cpu_baseline(wl, target_s=10.0):
     oracle.build(force=False)
     a_bits = wl.y.detach().view(wl.torch.int16).cpu().numpy().view(np.uint16)
     threads = oracle.default_threads()
-    rows = 16
-    t0 = time.perf_counter()
-    oracle.matmul(a_bits, wl.w_bits, rows=range(rows), threads=threads)
-    dt = time.perf_counter() - t0
-    # scale the sample to about target_s seconds of CPU work
-    rows = int(min(M, max(16, rows * target_s / max(dt, 1e-3))))
-    t0 = time.perf_counter()
-    oracle.matmul(a_bits, wl.w_bits, rows=range(rows), threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+    rows, v, dt = _timed(lambda n: oracle.matmul(a_bits, wl.w_bits, rows=range(n),
+                                                 threads=threads),
+                         lambda n: 2.0 * n * N * K / 1e12, target_s, M)
+    return {"value": v, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d rows of the [%d,%d]x[%d,%d] matmul, fp64, %.1f s" %
                       (rows, M, M, K, K, N, dt)}
 
@@ -479,6 +756,12 @@ def main():
                     help="skip the comparator timings and the invariance check")
     ap.add_argument("--no-e2e", action="store_true",
                     help="skip the end-to-end Llama-8B-shaped invariance run")
+    ap.add_argument("--no-sweeps", action="store_true",
+                    help="skip the size sweeps and the measured ceilings")
+    ap.add_argument("--only", choices=("sweeps", "ceilings"),
+                    help="run only the size sweeps or the ceilings and print them")
+    ap.add_argument("--sweep-parts", default="matmul,rmsnorm,decode,prefill",
+                    help="with --only sweeps: which sweeps, comma-separated")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -492,8 +775,14 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.only == "ceilings":
+        print(json.dumps({"ceilings": ceilings()}))
+        return
     log("bench: generating inputs")
     wl = Workload()
+    if args.only == "sweeps":
+        print(json.dumps({"sweeps": sweeps(wl, tuple(args.sweep_parts.split(",")))}))
+        return
     log("bench: warmup %d, timing %d steps" % (args.warmup, args.steps))
     torch.cuda.synchronize()
     wall, per = time_steps(wl, args.steps, args.warmup)
@@ -519,6 +808,16 @@ def main():
         extras["cost_of_invariance"] = comparators(wl)
         log("bench: other sizes")
         extras["more_sizes"] = more_sizes(wl)
+        if not args.no_sweeps:
+            log("bench: measured ceilings")
+            extras["ceilings"] = ceilings()
+            c = extras["ceilings"]
+            extras["vs_measured_ceilings"] = {
+                "matmul_over_mfma_loop": tflops / c["mfma_bf16_loop"]["TFLOP/s"],
+                "decode_over_read_stream": comp["attn_decode"]["GB/s"] / c["read_4GiB"]["GB/s"],
+                "rmsnorm_over_copy": comp["rmsnorm"]["GB/s"] / c["copy_4GiB"]["GB/s"]}
+            log("bench: size sweeps")
+            extras["sweeps"] = sweeps(wl)
         if not args.no_e2e:
             log("bench: end-to-end Llama-8B-shaped stack, alone vs 63 companions")
             extras["e2e_llama8b"] = e2e_llama8b()
@@ -526,6 +825,9 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: oracle on the host")
         cpu = cpu_baseline(wl)
+        if not args.no_extras:
+            log("bench: oracle on all cores and on one")
+            extras["cpu_oracle"] = cpu_oracle(wl)
     traffic = traffic_for("matmul.hip")
     line = {
         "metric": "invariant matmul TFLOP/s + RMSNorm/attn GB/s (% roofline), bitwise row-invariance",

@@ -204,6 +204,20 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
                             int32_t max_kv_len, int32_t num_splits, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* bix_mfma_loop: measurement only, the MFMA ceiling.  `workgroups` workgroups
+ * of four waves each run `iters` rounds of four independent bf16
+ * v_mfma_f32_32x32x16 chains on register operands: 4 * 32768 * iters flops
+ * per wave, no memory traffic.  sink: device float, written never (it only
+ * keeps the work from being optimised away). */
+int bix_mfma_loop(int64_t iters, int32_t workgroups, float* sink, void* stream);
+
+/* bix_read_stream: measurement only, the HBM read ceiling.  Reads `bytes`
+ * (a multiple of 16) from device pointer p (16-byte aligned) once, in 16-byte
+ * loads from `workgroups` workgroups of 256 lanes.  sink: device uint32,
+ * written never.  INVALID_SHAPE for a misaligned pointer or size. */
+int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
+                    void* stream);
+
 /* ---- Decoder-stack element-wise operations ---------------------------------
  * The rest of a dense Llama-style decoder layer around the three kernels
  * above, so that a whole stack can be run and its greedy output checked.  The

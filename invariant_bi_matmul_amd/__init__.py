@@ -21,7 +21,8 @@ __all__ = [
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
-    "attn_prefill_i16", "attn_decode_i16",
+    "attn_prefill_i16", "attn_decode_i16", "bix_mfma_loop",
+    "bix_read_stream",
 ]
 
 SPLIT = 256
@@ -86,6 +87,8 @@ def load():
         "bi_swiglu": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_add": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_argmax": (ctypes.c_int, [P, P, i64, i64, P]),
+        "bix_mfma_loop": (ctypes.c_int, [i64, i32, P, P]),
+        "bix_read_stream": (ctypes.c_int, [P, i64, i32, P, P]),
         "bi_attn_prefill_i16": (ctypes.c_int,
                                 [SP, P, P, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
         "bi_attn_decode_i16": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P]),
@@ -491,3 +494,28 @@ def attn_decode_i16(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, k_sc
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(lse),
         _stream()))
     return (o, lse) if lse is not None else o
+
+
+# --------------------------------------------------------------------------- measurement
+
+def bix_mfma_loop(iters: int, workgroups: int, sink: Optional[torch.Tensor] = None):
+    """Measurement only: ``workgroups`` x 4 waves each run ``iters`` rounds of four
+    independent bf16 32x32x16 MFMAs in registers.  Returns the flop count."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    _check("bix_mfma_loop", load().bix_mfma_loop(int(iters), int(workgroups), _ptr(sink),
+                                                 _stream()))
+    return 4.0 * 4 * 32768 * iters * workgroups
+
+
+def bix_read_stream(x: torch.Tensor, workgroups: int, sink: Optional[torch.Tensor] = None):
+    """Measurement only: read every byte of the contiguous device tensor ``x``
+    once.  Returns the byte count."""
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=x.device)
+    nbytes = x.numel() * x.element_size()
+    _check("bix_read_stream", load().bix_read_stream(_ptr(x), nbytes, int(workgroups), _ptr(sink),
+                                                     _stream()))
+    return nbytes

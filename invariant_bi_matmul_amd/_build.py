@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbi.so")
-SOURCES = ["rmsnorm.hip", "matmul.hip", "attention.hip", "model.hip", "api.cpp"]
+SOURCES = ["rmsnorm.hip", "matmul.hip", "attention.hip", "model.hip", "measure.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -348,6 +348,33 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
   }
 }
 
+// ---- measurement ---------------------------------------------------------------
+
+int bix_mfma_loop(int64_t iters, int32_t workgroups, float* sink, void* stream) {
+  try {
+    if (iters < 0 || workgroups < 0) return BI_ERR_INVALID_SHAPE;
+    if (iters == 0 || workgroups == 0) return BI_OK;
+    if (sink == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned4(sink)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_mfma_loop(iters, workgroups, sink, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
+                    void* stream) {
+  try {
+    if (bytes < 0 || workgroups < 0 || bytes % 16 != 0) return BI_ERR_INVALID_SHAPE;
+    if (bytes == 0 || workgroups == 0) return BI_OK;
+    if (p == nullptr || sink == nullptr) return BI_ERR_NULL_POINTER;
+    if (((uintptr_t)p & 15) != 0 || !aligned4(sink)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_read_stream(p, bytes, workgroups, sink, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
 // ---- int16 KV cache -----------------------------------------------------------
 
 int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,

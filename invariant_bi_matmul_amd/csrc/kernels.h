@@ -21,6 +21,9 @@ constexpr int kMatmulBK = 64;
 hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
                          int64_t k, hipStream_t st);
 int matmul_splitk_auto(int64_t m, int64_t n, int64_t k);
+hipError_t launch_mfma_loop(int64_t iters, int workgroups, float* sink, hipStream_t st);
+hipError_t launch_read_stream(const void* p, int64_t bytes, int workgroups, uint32_t* sink,
+                              hipStream_t st);
 hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,
                                 int64_t n, int64_t k, int split_k, float* ws, hipStream_t st);
 

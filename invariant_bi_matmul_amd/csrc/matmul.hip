@@ -33,6 +33,14 @@
 // columns), so the 32 workgroups resident on one XCD share a 4 x 8 block of A
 // rows and W columns in that XCD's L2.
 //
+// When every tile is the single row-tile (M <= 256), the waves skip the MFMAs
+// of their 32-row blocks that hold no row below M, and the A loads that would
+// only fill rows past M are not issued: per k-tile one A load (M <= 64), two
+// (M <= 128) or all four.  The LDS this frees deepens the ring (6 stages of
+// 24 KiB, 4 of 32 KiB, or 3 of 48 KiB), so a small-M launch, which only
+// streams W, keeps more of it in flight.  None of this touches a row's
+// arithmetic: the same MFMAs in the same k order produce every stored row.
+//
 // bix_matmul_* is the non-invariant comparator from the problem column of the
 // same row: split-K with a split count chosen from the grid size (so from M),
 // fp32 partials summed by a second kernel.
@@ -62,6 +70,12 @@ struct Tile {
   static_assert(MI * 32 == WM && NI * 32 == WN, "wave tile");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS");
   static_assert(LOADS <= 63, "vmcnt range");
+  // A variant that issues only the first NA of the A loads (single row-tile,
+  // M <= 64 NA) keeps NA * 8 KiB of A per stage and deepens the ring to what
+  // the same LDS holds: 6 stages for NA = 1, 4 for NA = 2, 3 for NA = 4.
+  static constexpr int a_bytes(int na) { return na * NT * 16; }
+  static constexpr int stage_bytes(int na) { return a_bytes(na) + W_BYTES; }
+  static constexpr int ring(int na) { return STAGES * STAGE / stage_bytes(na); }
 };
 
 // A in LDS: [BM rows][8 chunks of 16 B]; chunk c of row r sits at
@@ -99,7 +113,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
                                                              int K, int out_f32, int kt_per_split) {
   using T = Tile;
   constexpr int BK = T::BK, NT = T::NT, KS = T::KS, STAGES = T::STAGES;
-  constexpr int MI = T::MI, NI = T::NI, STAGE = T::STAGE, A_BYTES = T::A_BYTES;
+  constexpr int MI = T::MI, NI = T::NI, STAGE = T::STAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
 
   const int tiles_m = (M + T::BM - 1) / T::BM;
@@ -251,19 +265,21 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
     }
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  // loads [lo, hi) of the cursor's k-tile (A loads first, then W) into `stage`
-  auto issue = [&](int stage, int lo, int hi) __attribute__((always_inline)) {
+  // loads [lo, hi) of the cursor's k-tile into `stage`: the first NA A loads
+  // (load i fills A rows 64i .. 64i+63 of the stage), then the W loads.
+  auto issue = [&](int stage, int lo, int hi, auto nc) __attribute__((always_inline)) {
+    constexpr int NA = decltype(nc)::value;
     const int kt = kt0 + ikt;
     const uint8_t* ab = a_base + (int64_t)kt * (BK * 2);
     const uint8_t* wb = w_base + (int64_t)kt * BK * N * 2;
-    const uint32_t sb = lds0 + stage * STAGE + wave * 1024;
+    const uint32_t sb = lds0 + stage * T::stage_bytes(NA) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i)
+    for (int i = 0; i < NA; ++i)
       if (i >= lo && i < hi) lds_dma16_sv(ab, a_off[i], sb + i * NT * 16);
 #pragma unroll
     for (int i = 0; i < T::W_LOADS; ++i)
-      if (T::A_LOADS + i >= lo && T::A_LOADS + i < hi)
-        lds_dma16_sv(wb, w_off[i], sb + A_BYTES + i * NT * 16);
+      if (NA + i >= lo && NA + i < hi)
+        lds_dma16_sv(wb, w_off[i], sb + T::a_bytes(NA) + i * NT * 16);
   };
 
   // Per-thread LDS read offsets within a stage.
@@ -287,19 +303,24 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   for (int ni = 0; ni < NI; ++ni) {
     const int nb = wave_n * T::WN + ni * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
     const int k = 8 * (g16 >> 1) + (i16 >> 2);
-    wo[ni] = (uint32_t)(A_BYTES + k * T::W_ROW + (((nb >> 3) ^ swz_w(k)) << 4) + (nb & 7) * 2);
+    wo[ni] = (uint32_t)(k * T::W_ROW + (((nb >> 3) ^ swz_w(k)) << 4) + (nb & 7) * 2);
   }
 
-  auto frags = [&](const uint8_t* S, int kk, bf16x8 (&af)[MI], bf16x8 (&bw)[NI]) __attribute__((always_inline)) {
+  // fragments of k-step kk from the stage at S: the first NB row blocks of A
+  // and all of B (whose part starts after the variant's NA A loads)
+  auto frags_n = [&](const uint8_t* S, int kk, bf16x8 (&af)[MI], bf16x8 (&bw)[NI], auto nb,
+                     auto nc) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value, NA = decltype(nc)::value;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) af[mi] = as_bf16x8(*(const u32x4*)(S + ao[kk][mi]));
+    for (int mi = 0; mi < NB; ++mi) af[mi] = as_bf16x8(*(const u32x4*)(S + ao[kk][mi]));
+    const uint8_t* Sw = S + T::a_bytes(NA);
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       s16x4 v[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(S + wo[ni] + (16 * kk + 4 * h) * T::W_ROW));
+            (lds_s16x4*)(Sw + wo[ni] + (16 * kk + 4 * h) * T::W_ROW));
       bw[ni] = join_tr(v[0], v[1]);
     }
   };
@@ -318,9 +339,10 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   // MFMAs run under the reads of j+1's step 0, and group 0 of k-tile j+3 goes
   // out into stage S at once.
   bf16x8 fa[2][MI], fb[2][NI];
-  constexpr int GRP = (T::LOADS + KS - 1) / KS;  // loads per group
-  auto issue_group = [&](int stage, int g) __attribute__((always_inline)) {
-    issue(stage, g * GRP, min((g + 1) * GRP, T::LOADS));
+  auto issue_group = [&](int stage, int g, auto nc) __attribute__((always_inline)) {
+    constexpr int LOADS = decltype(nc)::value + T::W_LOADS;
+    constexpr int GRP = (LOADS + KS - 1) / KS;  // loads per group
+    issue(stage, g * GRP, min((g + 1) * GRP, LOADS), nc);
   };
   // Rows past M are never stored, and MFMA rows do not interact, so when every
   // tile is the single row-tile (M <= BM), the MFMAs (and A reads) of a wave's
@@ -328,48 +350,42 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   // variant with this wave's LIVE blocks throughout.  A row's bits stay those
   // of the full tile (same instruction, same k order); at small M the tile
   // then streams W instead of computing padding.
+  // In the same case the A loads that would fill only rows past M are not
+  // issued either: NA = 1 (M <= 64), 2 (M <= 128) or all 4 A loads per k-tile.
+  // Every row an MFMA of a live block reads lies below 64 * ceil(M / 64).
   static_assert(MI == 2, "the live-block variants assume two 32-row blocks per wave");
-  int live = MI;
+  static_assert(T::A_LOADS == 4 && T::BM / T::A_LOADS == 64, "A load i fills rows 64i..64i+63");
+  int live = MI, na = T::A_LOADS;
   if (tiles_m == 1) {
     const int rows = M - wave_m * T::WM;
     live = __builtin_amdgcn_readfirstlane(rows <= 0 ? 0 : (rows >= MI * 32 ? MI : (rows + 31) / 32));
+    na = M <= 64 ? 1 : (M <= 128 ? 2 : T::A_LOADS);
   }
   // the fragments of step kk for the first LIVE row blocks (all of B if any)
   auto frags_live = [&](const uint8_t* S, int kk, bf16x8 (&af)[MI], bf16x8 (&bw)[NI],
-                        auto lc) __attribute__((always_inline)) {
-    constexpr int LIVE = decltype(lc)::value;
-    if constexpr (LIVE == MI) {
-      frags(S, kk, af, bw);
-    } else if constexpr (LIVE > 0) {
-#pragma unroll
-      for (int mi = 0; mi < LIVE; ++mi) af[mi] = as_bf16x8(*(const u32x4*)(S + ao[kk][mi]));
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        s16x4 v[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(S + wo[ni] + (16 * kk + 4 * h) * T::W_ROW));
-        bw[ni] = join_tr(v[0], v[1]);
-      }
-    }
+                        auto lc, auto nc) __attribute__((always_inline)) {
+    if constexpr (decltype(lc)::value > 0) frags_n(S, kk, af, bw, lc, nc);
   };
-  auto ktile_body = [&](auto sc, auto lc) __attribute__((always_inline)) {
+  // One k-tile in stage S of a ring of R = ring(NA) stages.
+  auto ktile_body = [&](auto sc, auto lc, auto nc) __attribute__((always_inline)) {
     constexpr int S = decltype(sc)::value, LIVE = decltype(lc)::value;
-    const uint8_t* Sp = smem + S * STAGE;
-    const uint8_t* Snext = smem + ((S + 1) % STAGES) * STAGE;
-    constexpr int sn = (S + STAGES - 1) % STAGES;
+    constexpr int NA = decltype(nc)::value, LOADS = NA + T::W_LOADS, R = T::ring(NA);
+    constexpr int SB = T::stage_bytes(NA);
+    const uint8_t* Sp = smem + S * SB;
+    const uint8_t* Snext = smem + ((S + 1) % R) * SB;
+    constexpr int sn = (S + R - 1) % R;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KS) {
-        frags_live(Sp, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], lc);
+        frags_live(Sp, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1], lc, nc);
       } else {
-        wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
+        wait_vmcnt_le<(R - 2) * LOADS>();
         __syncthreads();  // next k-tile visible; every wave is done with this stage
         __builtin_amdgcn_sched_barrier(0);
         // all of them: the next k-tile may start a tile with more live rows
-        frags(Snext, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        frags_n(Snext, 0, fa[(kk + 1) & 1], fb[(kk + 1) & 1], std::integral_constant<int, MI>{},
+                nc);
       }
 #pragma unroll
       for (int mi = 0; mi < LIVE; ++mi)
@@ -384,16 +400,16 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kk + 1 < KS) {
-        issue_group(sn, kk + 1);
+        issue_group(sn, kk + 1, nc);
         if (kk + 2 == KS) advance();
       } else {
-        issue_group(S, 0);
+        issue_group(S, 0, nc);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto ktile = [&](auto sc, auto lc) __attribute__((always_inline)) {
-    ktile_body(sc, lc);
+  auto ktile = [&](auto sc, auto lc, auto nc) __attribute__((always_inline)) {
+    ktile_body(sc, lc, nc);
     if (++ckt == nk) {  // the tile is complete
       store_tile(cm0, cn0, acc);
 #pragma unroll
@@ -405,37 +421,49 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
     }
   };
   if (count == 0) return;
+  // The main loop is unrolled by the ring depth, so every stage offset is an
+  // immediate.
+  auto run = [&](auto lc, auto nc) __attribute__((always_inline)) {
+    constexpr int NA = decltype(nc)::value, LOADS = NA + T::W_LOADS, R = T::ring(NA);
+    static_assert(R >= 3 && R * T::stage_bytes(NA) <= STAGES * STAGE, "ring");
+    static_assert((R - 2) * LOADS <= 63, "vmcnt range");
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    issue(s, 0, T::LOADS);
-    advance();
-  }
-  // the first k-tile: wait for it, publish it, read its step 0; stage 2 is
-  // free, so group 0 of k-tile 2 goes out
-  wait_vmcnt_le<(STAGES - 2) * T::LOADS>();
-  __syncthreads();
-  frags(smem, 0, fa[0], fb[0]);
-  issue_group(STAGES - 1, 0);
-  static_assert(STAGES == 3, "the loop below is unrolled by the ring depth");
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  auto run = [&](auto lc) __attribute__((always_inline)) {
-    int64_t p = 0;
-    for (; p + 3 <= total; p += 3) {
-      ktile(S0{}, lc);
-      ktile(S1{}, lc);
-      ktile(S2{}, lc);
+    for (int s = 0; s < R - 1; ++s) {
+      issue(s, 0, LOADS, nc);
+      advance();
     }
-    if (p < total) ktile(S0{}, lc);
-    if (p + 1 < total) ktile(S1{}, lc);
+    // the first k-tile: wait for it, publish it, read its step 0; the last
+    // stage is free, so group 0 of k-tile R-1 goes out
+    wait_vmcnt_le<(R - 2) * LOADS>();
+    __syncthreads();
+    frags_n(smem, 0, fa[0], fb[0], std::integral_constant<int, MI>{}, nc);
+    issue_group(R - 1, 0, nc);
+    int64_t p = 0;
+    for (; p + R <= total; p += R)
+      static_for<0, R>([&](auto sc) __attribute__((always_inline)) { ktile(sc, lc, nc); });
+    static_for<0, R - 1>([&](auto sc) __attribute__((always_inline)) {
+      if (p + decltype(sc)::value < total) ktile(sc, lc, nc);
+    });
   };
-  if (live == MI)
-    run(std::integral_constant<int, MI>{});
-  else if (live == 1)
-    run(std::integral_constant<int, 1>{});
-  else
-    run(std::integral_constant<int, 0>{});
+  // one variant for the whole launch: (live blocks of this wave, A loads)
+  auto run_live = [&](auto nc) __attribute__((always_inline)) {
+    if (live == MI)
+      run(std::integral_constant<int, MI>{}, nc);
+    else if (live == 1)
+      run(std::integral_constant<int, 1>{}, nc);
+    else
+      run(std::integral_constant<int, 0>{}, nc);
+  };
+  if constexpr (SPLIT) {  // the comparator keeps the one full ring
+    run_live(std::integral_constant<int, T::A_LOADS>{});
+  } else {
+    if (na == 1)
+      run_live(std::integral_constant<int, 1>{});
+    else if (na == 2)
+      run_live(std::integral_constant<int, 2>{});
+    else
+      run_live(std::integral_constant<int, T::A_LOADS>{});
+  }
   wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
 }
 

@@ -48,7 +48,9 @@ def test_row_invariance_across_m(n):
     a, w = synth.matmul_inputs(2048, n, 4096, seed=2)
     wd = to_dev(w)
     full = _mm(a, None, w_dev=wd)
-    for m in M_SET[:-1]:
+    # the workload's M, and M on both sides of the single-row-tile variants
+    # (A loads for rows 0..63, 0..127, all 256)
+    for m in list(M_SET[:-1]) + [33, 65, 100, 128, 129, 200, 255, 257]:
         c = _mm(a[:m], None, w_dev=wd)
         assert np.array_equal(c, full[:m]), m
     # a row at many different positions inside tiles and batches
@@ -89,7 +91,8 @@ def test_one_hot_rows_select_w():
     assert np.all(c0 == 0.0) and not np.signbit(c0).any()
 
 
-@pytest.mark.parametrize("m,n,k", [(5, 8, 64), (33, 264, 128), (257, 520, 192), (1, 4104, 256)])
+@pytest.mark.parametrize("m,n,k", [(5, 8, 64), (33, 264, 128), (257, 520, 192), (1, 4104, 256),
+                                   (100, 264, 320), (64, 136, 64)])
 def test_ragged_shapes(orc, m, n, k):
     a, w = synth.matmul_inputs(m, n, k, seed=5)
     c = _mm(a, w)
