@@ -16,7 +16,7 @@
 //     either way.  Operands always come from LDS with the same layout; only
 //     how they get there differs: decode streams each wave's split through a
 //     wave-private ring of 5 chunk slots (RingSrc), prefill copies a whole
-//     split into LDS for the four waves of a workgroup to share (StagedSrc).
+//     split into LDS for the waves of a workgroup to share (StagedSrc).
 //     Both copy with direct global->LDS loads whose page is wave-uniform.
 //
 // Work unit: one wave64 computes the partial of one split for NB blocks of 16
@@ -975,12 +975,17 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
 }
 
 // ---- prefill -----------------------------------------------------------------
-// Grid (query tiles, kv heads, sequences); 4 waves per workgroup, each wave NB
-// blocks of 16/group positions x group heads.  Tiles run latest-first.  Each
-// 256-key split is copied into LDS (K, then V, by direct global->LDS loads)
-// and shared by the four waves: V(s) loads while K(s) is used, K(s+1) while
-// V(s) is used.
-constexpr int kPrefillNB = 1;
+// Grid (query tiles, kv heads, sequences); WAVES waves per workgroup, each
+// wave NB blocks of 16/group positions x group heads.  Tiles run latest-first.
+// Each 256-key split is copied into LDS (K, then V, by direct global->LDS
+// loads) and shared by the workgroup's waves: V(s) loads while K(s) is used,
+// K(s+1) while V(s) is used.  The two splits' rows fill most of a CU's LDS, so
+// one workgroup runs per CU.  A launch with enough queries uses 8 waves (two
+// per SIMD, whose MFMAs and softmax arithmetic then overlap, and each staged
+// split serves twice the queries); a small one uses 4 waves so that its few
+// queries still spread over all CUs.  A block's arithmetic is the same in
+// every shape (the same MFMAs in the same order on the same operands), so a
+// query's output bits depend on neither.
 
 // Copy the K or V rows of a whole 256-key split into LDS: thread t's load n
 // fills the 1 KiB block n*4 + t/64 (one page is 16 keys = 4 KiB at d=128,
@@ -1024,13 +1029,16 @@ struct SplitFactors {
   const int32_t* bt_row = nullptr;
 };
 
-template <int D, bool IS_K>
+// WAVES waves share the copy: load n of wave w brings keys (WAVES*n + w)*KPI
+// .. +KPI-1, which lie in page (WAVES*n*KPI)/16 + (w*KPI)/16 of the split.
+template <int D, bool IS_K, int WAVES>
 __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPages& sp, int nkv,
                                             int g, int key0, int last, uint8_t* lds,
                                             const StageLaneOffs<D>& offs,
                                             const SplitFactors& fac = SplitFactors{}) {
   constexpr int KPI = kWave / KV<D>::CPR;       // keys per 1 KiB load
-  constexpr int NLOAD = 256 / KPI / 4;          // loads per thread (4 waves)
+  constexpr int NLOAD = 256 / KPI / WAVES;      // loads per thread
+  static_assert((WAVES * KPI) % 16 == 0 && KPI <= 16, "a load stays inside one page");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (IS_K && fac.kf != nullptr) {
     // before the row loads: the block-table read is waited for here, with no
@@ -1038,7 +1046,16 @@ __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPag
     if (wave == 0) stage_factors(fac.kf, fac.bt_row, key0, last, nkv, g, fac.klds);
     if (wave == 1) stage_factors(fac.vf, fac.bt_row, key0, last, nkv, g, fac.vlds);
   }
-  const bool hi = ((wave * KPI) >> 4) != 0;     // the wave's keys start in the next page
+  const int poff = (wave * KPI) >> 4;           // pages the wave's first key is past
+  auto page_of = [&](int pidx) __attribute__((always_inline)) {
+    if constexpr (WAVES * KPI <= 32) {           // poff is 0 or 1
+      return poff != 0 ? sp.pg[min(pidx + 1, 15)] : sp.pg[pidx];
+    } else {                                     // poff is 0..3
+      const int a = poff & 1 ? sp.pg[min(pidx + 1, 15)] : sp.pg[pidx];
+      const int b = poff & 1 ? sp.pg[min(pidx + 3, 15)] : sp.pg[min(pidx + 2, 15)];
+      return poff & 2 ? b : a;
+    }
+  };
   const uint32_t base = (uint32_t)(uintptr_t)lds;
   if (key0 + kSplit - 1 <= last) {
     const uint16_t* pool_g = pool + (int64_t)g * 16 * D;
@@ -1046,34 +1063,32 @@ __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPag
     const uint32_t wbase = base + (uint32_t)(wave * KPI * KV<D>::ROWB);
     static_for<0, NLOAD>([&](auto nc) {
       constexpr int n = decltype(nc)::value;
-      constexpr int pidx = (n * 4 * KPI) >> 4;
-      const int page = (hi && pidx + 1 < 16) ? sp.pg[pidx + 1] : sp.pg[pidx];
-      constexpr int h = ((n * 4 * KPI) >> 4) & 1;
-      lds_dma16_si<n * 4 * KPI * KV<D>::ROWB>(page_block(pool_g, page, page_elems),
-                                              IS_K ? offs.k[h] : offs.v[h], wbase);
+      constexpr int pidx = (n * WAVES * KPI) >> 4;
+      constexpr int h = ((n * WAVES * KPI) >> 4) & 1;
+      lds_dma16_si<n * WAVES * KPI * KV<D>::ROWB>(page_block(pool_g, page_of(pidx), page_elems),
+                                                  IS_K ? offs.k[h] : offs.v[h], wbase);
     });
     return;
   }
 #pragma unroll
   for (int n = 0; n < NLOAD; ++n) {
-    const int pidx = (n * 4 * KPI) >> 4;        // compile-time after unrolling
-    const int page = (hi && pidx + 1 < 16) ? sp.pg[pidx + 1] : sp.pg[pidx];
-    const int kfirst = (n * 4 + wave) * KPI;
-    dma_block<D, IS_K>(pool, page, nkv, g, key0, kfirst, last,
+    const int pidx = (n * WAVES * KPI) >> 4;    // compile-time after unrolling
+    const int kfirst = (n * WAVES + wave) * KPI;
+    dma_block<D, IS_K>(pool, page_of(pidx), nkv, g, key0, kfirst, last,
                        base + (uint32_t)kfirst * KV<D>::ROWB);
   }
 }
 
 // Q16: the cache holds int16 rows with per-(page, kv head, slot) factors
 // kf / vf (nullptr otherwise).  cu_q == nullptr means one token per sequence.
-template <int D, bool Q16>
-__global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
+template <int D, bool Q16, int NB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void bi_attn_prefill_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ kv_len, const int32_t* __restrict__ bt,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc, uint16_t* __restrict__ out,
     float* __restrict__ lse, int nq, int nkv, int max_pages, float c2,
     const float* __restrict__ kf, const float* __restrict__ vf) {
-  constexpr int NB = kPrefillNB, DB = KV<D>::DB;
+  constexpr int DB = KV<D>::DB;
   __shared__ __attribute__((aligned(1024))) uint8_t klds[256 * KV<D>::ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t vlds[256 * KV<D>::ROWB];
   __shared__ __attribute__((aligned(1024))) uint8_t flds[Q16 ? 2 * 1024 : 16];
@@ -1083,7 +1098,7 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   const int tile = (int)(gridDim.x - 1 - blockIdx.x);
   const int group = nq / nkv;
   const int ppb = 16 / group;  // positions per block
-  const int per_wg = 4 * NB * ppb;
+  const int per_wg = WAVES * NB * ppb;
   const int tok0 = cu_q != nullptr ? cu_q[b] : b;
   const int nb = cu_q != nullptr ? cu_q[b + 1] - tok0 : 1;
   if (tile * per_wg >= nb) return;  // whole workgroup: no barrier reached
@@ -1132,12 +1147,12 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
   pages.load(bt_row, 0, L - 1);
   StageLaneOffs<D> soffs;
   soffs.init(wave);
-  stage_split<D, true>(kc, pages, nkv, g, 0, L - 1, klds, soffs, fac);
+  stage_split<D, true, WAVES>(kc, pages, nkv, g, 0, L - 1, klds, soffs, fac);
   for (int s = 0; s < nsplit; ++s) {
     const int key0 = s * kSplit;
     wait_vmcnt_le<0>();
     __syncthreads();  // K(s) in LDS; every wave is done reading V(s-1)
-    stage_split<D, false>(vc, pages, nkv, g, key0, L - 1, vlds, soffs);
+    stage_split<D, false, WAVES>(vc, pages, nkv, g, key0, L - 1, vlds, soffs);
     SplitPages next;  // the next split's pages, fetched while this one computes
     if (s + 1 < nsplit) next.load(bt_row, key0 + kSplit, L - 1);
     u32x4 p[NB][8];
@@ -1147,7 +1162,7 @@ __global__ __launch_bounds__(256) void bi_attn_prefill_kernel(
     __syncthreads();  // V(s) in LDS; every wave is done reading K(s)
     if (s + 1 < nsplit) {
       pages = next;
-      stage_split<D, true>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs, fac);
+      stage_split<D, true, WAVES>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs, fac);
     }
     f32x4 os[NB][DB];
     split_pv<D, NB>(src, p, os);
@@ -1266,30 +1281,58 @@ hipError_t launch_kv_append(const AttnDims& s, const void* k_new, const void* v_
   return hipGetLastError();
 }
 
+// The wide prefill workgroup: NB blocks per wave x WAVES waves (NB * WAVES = 8).
+constexpr int kWideNB = 1, kWideWaves = 8;
+
+// Compute units of the current device (256 on MI355X), asked once.
+static int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* cu_q,
                                const int32_t* kv_len, const int32_t* bt, const void* kc,
                                const void* vc, void* out, float* lse, int max_q_per_seq,
                                hipStream_t st, const float* kf, const float* vf) {
-  const int per_wg = 4 * kPrefillNB * (16 / (s.nq / s.nkv));
+  const bool q16 = kf != nullptr;
+  // A wide workgroup (8 waves of one block, or 4 waves of two) covers 32
+  // positions; it is used (bf16 cache) when that still gives >= 4 workgroups
+  // per CU: with fewer, the causal triangle's longest tiles decide the time and
+  // the coarser split of the work costs what the wider tile saves.
+  const int ppb = 16 / (s.nq / s.nkv);
+  const int64_t wide_wgs = (int64_t)((max_q_per_seq + 8 * ppb - 1) / (8 * ppb)) * s.nkv * s.B;
+  const bool wide = !q16 && wide_wgs >= 4 * (int64_t)device_cus();
+  const int per_wg = (wide ? 8 : 4) * ppb;
   const dim3 grid((unsigned)((max_q_per_seq + per_wg - 1) / per_wg), (unsigned)s.nkv,
                   (unsigned)s.B);
   const float c2 = base2_scale(s.scale);
-  const bool q16 = kf != nullptr;
-#define BI_PREFILL(DD, QQ)                                                                     \
-  hipLaunchKernelGGL((bi_attn_prefill_kernel<DD, QQ>), grid, dim3(256), 0, st,                 \
+#define BI_PREFILL(DD, QQ, NN, WW)                                                             \
+  hipLaunchKernelGGL((bi_attn_prefill_kernel<DD, QQ, NN, WW>), grid, dim3(64 * WW), 0, st,     \
                      (const uint16_t*)q, cu_q, kv_len, bt, (const uint16_t*)kc,                \
                      (const uint16_t*)vc, (uint16_t*)out, lse, s.nq, s.nkv, s.max_pages, c2, kf, \
                      vf)
   if (s.d == 128) {
     if (q16)
-      BI_PREFILL(128, true);
+      BI_PREFILL(128, true, 1, 4);
+    else if (wide)
+      BI_PREFILL(128, false, kWideNB, kWideWaves);
     else
-      BI_PREFILL(128, false);
+      BI_PREFILL(128, false, 1, 4);
   } else {
     if (q16)
-      BI_PREFILL(64, true);
+      BI_PREFILL(64, true, 1, 4);
+    else if (wide)
+      BI_PREFILL(64, false, kWideNB, kWideWaves);
     else
-      BI_PREFILL(64, false);
+      BI_PREFILL(64, false, 1, 4);
   }
 #undef BI_PREFILL
   return hipGetLastError();
@@ -1314,15 +1357,7 @@ hipError_t launch_kv_append_i16(const AttnDims& s, const void* k_new, const void
 // Workgroups of the persistent decode kernel: one per CU (each uses most of
 // a CU's LDS), fewer when there are fewer units.
 static int decode_workgroups(int64_t units) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
+  const int cus = device_cus();
   const int64_t need = (units + kDecodeWaves - 1) / kDecodeWaves;
   return (int)(need < cus ? need : cus);
 }

@@ -97,6 +97,24 @@ def test_gqa_4096_chunked_prefill_then_decode(orc):
         assert np.array_equal(run.out[b], one.out[b])
 
 
+@pytest.mark.parametrize("nq,nkv,d,L,B", [(8, 2, 64, 1024, 16), (4, 4, 64, 2048, 16),
+                                          (32, 8, 128, 1024, 8)])
+def test_wide_prefill_equals_narrow_chunks(orc, nq, nkv, d, L, B):
+    """A one-shot prefill with enough queries runs two query blocks per wave;
+    small chunks run one.  Both give the same bits, and match the oracle."""
+    lens, _ = synth.ragged_lengths(B, L, seed=3)
+    prob = synth.attn_problem(lens, n_q=nq, n_kv=nkv, d=d, seed=4)
+    wide = PagedRun(prob, page_seed=1)
+    wide.prefill([(b, n) for b, n in enumerate(lens)])
+    narrow = PagedRun(prob, page_seed=2)
+    narrow.run_chunked(64)
+    for b in range(B):
+        assert np.array_equal(wide.out[b], narrow.out[b]), b
+        assert np.array_equal(wide.lse[b].view(np.uint32), narrow.lse[b].view(np.uint32)), b
+    picks = [(b, p) for b in (0, B - 1) for p in (0, 255, 256, lens[b] - 1)]
+    _parity(orc, prob, wide, picks)
+
+
 def test_decode_batch_companions_and_position():
     """A probe sequence's decode rows are the same alone and among 15
     companions at any batch index, with different page placements."""
