@@ -371,6 +371,36 @@ def time_rotating(fns, reps):
     return a.elapsed_time(b) / reps
 
 
+def time_graph(fns, reps):
+    """Average ms per call of the same rotation replayed from one captured HIP
+    graph: the launches leave the host at once, so a short kernel is timed
+    without Python's per-call overhead.  None if capture fails."""
+    import torch
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fns[i % len(fns)]()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / reps
+    except Exception as e:  # capture is a measurement aid, never a failure
+        log("bench: graph capture failed: %s" % e)
+        return None
+
+
 ROTATE_BYTES = 512 << 20   # twice the 256 MiB MALL
 CUS = 256
 MFMA_FLOPS_PER_CU_CLK = 4096   # dense bf16: 2.5 PFLOP/s = 256 CUs x 4096 x 2.4 GHz
@@ -432,7 +462,9 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
     {1..16384 powers of two, 3, 7, 1000, 16383}, H in {4096, 8192}.  Decode:
     L in {512, 4096, 32768} x B in {1..64}, lengths ragged U{L/2..L} with one
     probe at L, shuffled 16-token pages.  Prefill: one sequence of L tokens,
-    one-shot against 512-token chunks (and whether they agree bit for bit)."""
+    one-shot against 512-token chunks (and whether they agree bit for bit).
+    Matmul, RMSNorm and decode are also timed replayed from a captured HIP
+    graph (graph_ms), which removes the host's per-call launch cost."""
     import torch
     bi, synth, dev, np = wl.bi, wl.synth, wl.dev, wl.np
     out = {"matmul": {}, "rmsnorm": {}, "decode": {}, "prefill": {}}
@@ -449,6 +481,7 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
             cs = [torch.empty(m, n, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
             fns = [(lambda w=w, c=c: bi.matmul(a, w, out=c)) for w, c in zip(ws, cs)]
             ms = time_rotating(fns, max(40, 2 * sets))
+            gms = time_graph(fns, max(40, 2 * sets))
             vfns = [(lambda w=w, c=c: torch.matmul(a, w, out=c)) for w, c in zip(ws, cs)]
             vms = time_rotating(vfns, max(40, 2 * sets))
             flops = 2.0 * m * n * K
@@ -460,7 +493,7 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
                 "ms": ms, "TFLOP/s": tf, "mfma_frac": tf / MFMA_BF16_PEAK,
                 "roofline_TFLOP/s": roof, "roofline_frac": tf / roof,
                 "GB/s": by / ms / 1e6, "tiles": tiles, "grid_fill_ceiling": _grid_fill(tiles),
-                "vendor_ms": vms, "invariant_over_vendor": ms / vms}
+                "vendor_ms": vms, "invariant_over_vendor": ms / vms, "graph_ms": gms}
             del cs
         del ws
     for h in (4096, 8192) if "rmsnorm" in parts else ():
@@ -474,9 +507,12 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
             fns = [(lambda i=i: bi.rmsnorm(xb[i * r:(i + 1) * r], g, wl.eps,
                                            out=yb[i * r:(i + 1) * r])) for i in range(sets)]
             ms = time_rotating(fns, max(20, sets))
+            gms = time_graph(fns, max(20, sets))
             by = 4.0 * h * r + 2 * h
             out["rmsnorm"]["R%d_H%d" % (r, h)] = {"ms": ms, "GB/s": by / ms / 1e6,
-                                                  "hbm_frac": by / ms / 1e6 / HBM_PEAK_GBS}
+                                                  "hbm_frac": by / ms / 1e6 / HBM_PEAK_GBS,
+                                                  "graph_ms": gms,
+                                                  "graph_GB/s": by / gms / 1e6 if gms else None}
         del xb, yb
     for L in (512, 4096, 32768) if "decode" in parts else ():
         log("sweep: decode L=%d" % L)
@@ -508,10 +544,12 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
             fns = [(lambda bt=bt: bi.attn_decode(q, kn, vn, kvl, bt, kc, vc, wl.scale, L,
                                                  workspace=wsp, out=o)) for bt in bts]
             ms = time_rotating(fns, max(20, sets))
+            gms = time_graph(fns, max(20, sets))
             by = set_bytes + bsz * NQ * D * 2 * 2 + bsz * NKV * D * 2 * 2
             out["decode"]["B%d_L%d" % (bsz, L)] = {"ms": ms, "GB/s": by / ms / 1e6,
                                                    "hbm_frac": by / ms / 1e6 / HBM_PEAK_GBS,
-                                                   "kv_tokens": sum(lens)}
+                                                   "kv_tokens": sum(lens), "graph_ms": gms,
+                                                   "graph_GB/s": by / gms / 1e6 if gms else None}
             del kc, vc, bts
     for L in (512, 4096, 32768) if "prefill" in parts else ():
         log("sweep: prefill L=%d" % L)
@@ -797,6 +835,16 @@ def main():
                          "TFLOP/s": w["prefill"]["flops"] / per["prefill"] / 1e9},
         "attn_decode": {"ms": per["decode"], "GB/s": w["decode"]["bytes"] / per["decode"] / 1e6},
     }
+    # the same stages replayed from a captured graph: the kernels' own time,
+    # without the events' and the host's per-launch gaps (short stages only
+    # differ)
+    for name, key, unit, work in (("rmsnorm", "rmsnorm", "GB/s", w["rmsnorm"]["bytes"] / 1e6),
+                                  ("matmul", "matmul", "TFLOP/s", w["matmul"]["flops"] / 1e9),
+                                  ("prefill", "attn_prefill", "TFLOP/s", w["prefill"]["flops"] / 1e9),
+                                  ("decode", "attn_decode", "GB/s", w["decode"]["bytes"] / 1e6)):
+        gms = time_graph([getattr(wl, name)], 20)
+        comp[key]["graph_ms"] = gms
+        comp[key]["graph_" + unit] = work / gms if gms else None
     comp["rmsnorm"]["hbm_frac"] = comp["rmsnorm"]["GB/s"] / HBM_PEAK_GBS
     comp["matmul"]["mfma_frac"] = tflops / MFMA_BF16_PEAK
     comp["attn_prefill"]["mfma_frac"] = comp["attn_prefill"]["TFLOP/s"] / MFMA_BF16_PEAK
