@@ -195,7 +195,7 @@ def test_repeat_bitwise():
             assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("B,maxlen", [(300, 600), (256, 2048)])
+@pytest.mark.parametrize("B,maxlen", [(300, 600), (256, 2048), (512, 300)])
 def test_decode_large_and_mixed_batches(orc, B, maxlen):
     """Decode over batches at and past the size the balanced unit list
     covers (256 sequences), with sequences from 1 to 8 splits: every decoded
