@@ -33,7 +33,17 @@
  *     nearest even.  Sizes of 0 are no-ops returning BI_OK; negative sizes are
  *     BI_ERR_INVALID_SHAPE.
  *   - Contents of device index arrays (kv_len, cu_q, block_table) are trusted:
- *     entries outside the documented ranges are undefined behaviour.
+ *     entries outside the documented ranges are undefined behaviour.  The
+ *     debug build of the library (libbi_debug.so, compiled with
+ *     BI_DEBUG_CHECKS) checks them on the device before each attention call
+ *     launches anything: 1 <= kv_len[b] <= the call's length bound (max_kv_len
+ *     for decode, max_pages_per_seq * page_size otherwise); cu_q starts at 0,
+ *     never decreases, gives each sequence at most max_q_per_seq and at most
+ *     kv_len[b] tokens and ends at total_q; every block-table entry a
+ *     sequence's length reaches is in [0, num_pages).  A violation returns
+ *     BI_ERR_INVALID_SHAPE with nothing else enqueued.  That build
+ *     synchronises the stream on every attention call, allocates one int per
+ *     device (once) for the result, and cannot be captured into a graph.
  *   - No C++ exception crosses this interface.
  *   - Tensor pointers must be 16-byte aligned (BI_ERR_INVALID_SHAPE otherwise).
  */

@@ -17,7 +17,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "BIError", "lib_path", "load", "abi_version", "rmsnorm", "matmul", "attn_workspace_bytes",
+    "BIError", "lib_path", "debug_lib_path", "load", "load_library", "abi_version", "rmsnorm",
+    "matmul", "attn_workspace_bytes",
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
@@ -58,9 +59,21 @@ def lib_path() -> str:
 def load():
     """Load libbi.so (once).  Raises if it is absent: there is no fallback."""
     global _lib
-    if _lib is not None:
-        return _lib
-    path = lib_path()
+    if _lib is None:
+        _lib = load_library(lib_path())
+    return _lib
+
+
+def debug_lib_path() -> str:
+    """The same library built with BI_DEBUG_CHECKS: its attention calls check
+    kv_len, cu_q and the block table on the device before they launch, and
+    return BI_ERR_INVALID_SHAPE for a bad entry (they synchronise the
+    stream to do so).  Select it with BI_LIB=<this path>."""
+    return os.path.join(_HERE, "libbi_debug.so")
+
+
+def load_library(path: str):
+    """A ctypes handle on the library at `path` with every signature set."""
     if not os.path.exists(path):
         raise RuntimeError("libbi.so not found at %s; build it with "
                            "`python -m invariant_bi_matmul_amd._build`" % path)
@@ -100,7 +113,6 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
 
 

@@ -20,7 +20,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbi.so")
-SOURCES = ["rmsnorm.hip", "matmul.hip", "attention.hip", "model.hip", "measure.hip", "api.cpp"]
+# the same library with BI_DEBUG_CHECKS: attention calls validate their index arrays first
+DEBUG_LIB = os.path.join(HERE, "libbi_debug.so")
+SOURCES = ["rmsnorm.hip", "matmul.hip", "attention.hip", "model.hip", "measure.hip", "checks.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -41,9 +44,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-I", INCLUDE, "-I", CSRC]
+def _compile(src: str, debug: bool = False) -> str:
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ("_debug" if debug else "") + ".o")
+    cmd = [hipcc()] + FLAGS + (["-DBI_DEBUG_CHECKS"] if debug else []) + ["-I", INCLUDE, "-I", CSRC]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -58,19 +61,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every source and link libbi.so in-tree.  Always rebuilds."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libbi.so and libbi_debug.so in-tree (the
+    debug library differs only in api.cpp).  Always rebuilds."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = [(src, False) for src in SOURCES] + [("api.cpp", True)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    release, debug_api = objs[:len(SOURCES)], objs[-1]
+    _link(release, LIB)
+    _link([o for o in release if not o.endswith(os.sep + "api.o")] + [debug_api], DEBUG_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", DEBUG_LIB)
     return LIB
 
 

@@ -3,6 +3,13 @@
 // Every entry point checks its host arguments completely before it enqueues
 // anything, then launches on the caller's stream.  Nothing here allocates,
 // synchronises or keeps state.
+//
+// Built with BI_DEBUG_CHECKS (libbi_debug.so), the attention entry points
+// also validate the device index arrays before they launch anything: a
+// check kernel reads kv_len, cu_q and the block table, the stream is
+// synchronised, and a bad entry returns BI_ERR_INVALID_SHAPE with nothing
+// else enqueued.  That build allocates one int per device for the result
+// (once) and cannot run under stream capture.
 #include "bi.h"
 
 #include <hip/hip_runtime.h>
@@ -40,6 +47,38 @@ bi::AttnDims dims_of(const bi_attn_shape* s) {
   return bi::AttnDims{s->num_seqs, s->num_q_heads, s->num_kv_heads, s->head_dim,
                       s->max_pages_per_seq, s->softmax_scale};
 }
+
+#ifdef BI_DEBUG_CHECKS
+// Validate the index arrays of an attention call (see checks.hip); BI_OK,
+// BI_ERR_INVALID_SHAPE, or BI_ERR_HIP.
+int debug_check_tables(const bi_attn_shape* s, const int32_t* kv_len, const int32_t* cu_q,
+                       const int32_t* bt, int max_len, int max_q, int64_t total_q,
+                       hipStream_t st) {
+  static int* flags[64] = {};  // one device int per device, allocated once
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BI_ERR_HIP;
+  if (flags[dev] == nullptr && hipMalloc((void**)&flags[dev], sizeof(int)) != hipSuccess)
+    return BI_ERR_HIP;
+  if (bi::launch_check_attn_tables(kv_len, cu_q, bt, s->num_seqs, s->max_pages_per_seq,
+                                   s->num_pages, max_len, max_q, total_q, flags[dev], st) !=
+      hipSuccess)
+    return BI_ERR_HIP;
+  int bad = 0;
+  if (hipMemcpyAsync(&bad, flags[dev], sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return BI_ERR_HIP;
+  return bad == 0 ? BI_OK : BI_ERR_INVALID_SHAPE;
+}
+#define BI_CHECK_TABLES(...)                          \
+  do {                                                \
+    const int chk = debug_check_tables(__VA_ARGS__); \
+    if (chk != BI_OK) return chk;                     \
+  } while (0)
+#else
+#define BI_CHECK_TABLES(...) \
+  do {                       \
+  } while (0)
+#endif
 
 size_t decode_ws_bytes(const bi_attn_shape* s, int64_t tokens, int64_t nsplit) {
   return (size_t)tokens * (size_t)s->num_q_heads * (size_t)nsplit *
@@ -197,6 +236,8 @@ int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, co
       return BI_ERR_INVALID_SHAPE;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
+    BI_CHECK_TABLES(s, kv_len, cu_q, block_table, s->max_pages_per_seq * s->page_size,
+                    max_q_per_seq, total_q, st);
     hipError_t e = bi::launch_kv_append(d, k_new, v_new, cu_q, kv_len, block_table, k_cache,
                                         v_cache, max_q_per_seq, st);
     if (e != hipSuccess) return BI_ERR_HIP;
@@ -241,6 +282,7 @@ int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, con
     if ((int64_t)s->num_seqs * s->num_kv_heads * ns / 4 + 1 > kMaxGridX) return BI_ERR_UNSUPPORTED;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
+    BI_CHECK_TABLES(s, kv_len, nullptr, block_table, max_kv_len, 1, 0, st);
     hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
                                         v_cache, 1, st);
     if (e != hipSuccess) return BI_ERR_HIP;
@@ -278,6 +320,7 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
       return BI_ERR_WORKSPACE_TOO_SMALL;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
+    BI_CHECK_TABLES(s, kv_len, nullptr, block_table, max_kv_len, 1, 0, st);
     hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
                                         v_cache, 1, st);
     if (e != hipSuccess) return BI_ERR_HIP;
@@ -400,6 +443,8 @@ int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new
       return BI_ERR_INVALID_SHAPE;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
+    BI_CHECK_TABLES(s, kv_len, cu_q, block_table, s->max_pages_per_seq * s->page_size,
+                    max_q_per_seq, total_q, st);
     hipError_t e = bi::launch_kv_append_i16(d, k_new, v_new, cu_q, kv_len, block_table, k_cache,
                                             v_cache, k_scale, v_scale, max_q_per_seq, st);
     if (e != hipSuccess) return BI_ERR_HIP;
@@ -428,6 +473,8 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
       return BI_ERR_INVALID_SHAPE;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
+    BI_CHECK_TABLES(s, kv_len, nullptr, block_table, s->max_pages_per_seq * s->page_size, 1, 0,
+                    st);
     hipError_t e = bi::launch_kv_append_i16(d, k_new, v_new, nullptr, kv_len, block_table,
                                             k_cache, v_cache, k_scale, v_scale, 1, st);
     if (e != hipSuccess) return BI_ERR_HIP;

@@ -22,6 +22,12 @@ hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int6
                          int64_t k, hipStream_t st);
 int matmul_splitk_auto(int64_t m, int64_t n, int64_t k);
 hipError_t launch_mfma_loop(int64_t iters, int workgroups, float* sink, hipStream_t st);
+
+// Debug-build validation of the attention index arrays: bits of *flag.
+constexpr int kCheckLength = 1, kCheckQueries = 2, kCheckPage = 4;
+hipError_t launch_check_attn_tables(const int32_t* kv_len, const int32_t* cu_q, const int32_t* bt,
+                                    int B, int max_pages, int64_t num_pages, int max_len,
+                                    int max_q, int64_t total_q, int* flag, hipStream_t st);
 hipError_t launch_read_stream(const void* p, int64_t bytes, int workgroups, uint32_t* sink,
                               hipStream_t st);
 hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,

@@ -34,6 +34,18 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_debug_build_exports_the_same_functions():
+    """libbi_debug.so (attention calls validate their device index arrays)
+    is the same interface."""
+    from invariant_bi_matmul_amd import _build
+    if not os.path.exists(_build.DEBUG_LIB):
+        pytest.fail("libbi_debug.so is not built (python -m invariant_bi_matmul_amd._build)")
+    dbg = ctypes.CDLL(_build.DEBUG_LIB)
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+    assert dbg.bi_abi_version() == 1
+
+
 def test_version_and_status_strings(lib):
     assert lib.bi_abi_version() == 1
     for s in range(7):
