@@ -408,7 +408,8 @@ MFMA_FLOPS_PER_CU_CLK = 4096   # dense bf16: 2.5 PFLOP/s = 256 CUs x 4096 x 2.4 
 
 def ceilings():
     """Measured ceilings beside the datasheet peaks: a 4 GiB device copy (read +
-    write), a 4 GiB read-only sweep (bix_read_stream), and an MFMA-only
+    write), a 4 GiB read-only stream through LDS (bix_read_stream, the decode
+    kernel's way of reading), and an MFMA-only
     register loop (bix_mfma_loop), whose rate over 4096 flop per CU per clock
     gives the clock the chip holds under matrix load."""
     import torch
@@ -422,7 +423,7 @@ def ceilings():
     del dst
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     best = None
-    for wg in (1024, 2048, 4096, 8192):
+    for wg in (256, 512, 1024):
         ms = time_call(lambda: bi.bix_read_stream(src, wg, sink), reps=5, warmup=1)
         gbs = 4 * n / ms / 1e6
         if best is None or gbs > best["GB/s"]:

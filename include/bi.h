@@ -222,8 +222,9 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
 int bix_mfma_loop(int64_t iters, int32_t workgroups, float* sink, void* stream);
 
 /* bix_read_stream: measurement only, the HBM read ceiling.  Reads `bytes`
- * (a multiple of 16) from device pointer p (16-byte aligned) once, in 16-byte
- * loads from `workgroups` workgroups of 256 lanes.  sink: device uint32,
+ * (a multiple of 8192) from device pointer p (16-byte aligned) once, as 8 KiB
+ * chunks streamed through LDS by direct loads (the decode kernel's way of
+ * reading), from `workgroups` workgroups of two waves.  sink: device uint32,
  * written never.  INVALID_SHAPE for a misaligned pointer or size. */
 int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
                     void* stream);

@@ -408,7 +408,7 @@ int bix_mfma_loop(int64_t iters, int32_t workgroups, float* sink, void* stream) 
 int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
                     void* stream) {
   try {
-    if (bytes < 0 || workgroups < 0 || bytes % 16 != 0) return BI_ERR_INVALID_SHAPE;
+    if (bytes < 0 || workgroups < 0 || bytes % 8192 != 0) return BI_ERR_INVALID_SHAPE;
     if (bytes == 0 || workgroups == 0) return BI_OK;
     if (p == nullptr || sink == nullptr) return BI_ERR_NULL_POINTER;
     if (((uintptr_t)p & 15) != 0 || !aligned4(sink)) return BI_ERR_INVALID_SHAPE;

@@ -7,9 +7,10 @@
 // of one 32-cycle MFMA each keep a chain's next MFMA 128 cycles behind its
 // previous one, past the instruction's latency.
 //
-// bix_read_stream_kernel gives the HBM read ceiling: a grid-stride sweep of
-// 16-byte loads, four in flight per lane, folded into one value that is
-// stored only if it is a pattern the sweep never produces.
+// bix_read_stream_kernel gives the HBM read ceiling the way the decode kernel
+// reads: each wave pulls 8 KiB chunks (chunks w, w + NW, ... of the buffer)
+// through a private LDS ring of 8 chunk slots by direct global->LDS loads,
+// seven chunks in flight, and touches one value of each landed chunk.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,26 +40,46 @@ __global__ __launch_bounds__(256) void bix_mfma_loop_kernel(int64_t iters, float
   if (t == 12345.0f) sink[0] = t;
 }
 
-__global__ __launch_bounds__(256) void bix_read_stream_kernel(const u32x4* __restrict__ p,
-                                                              int64_t n16, uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a ^ b ^ c ^ d;
+constexpr int kStreamChunk = 8192, kStreamRing = 8, kStreamWaves = 2;
+
+__global__ __launch_bounds__(64 * kStreamWaves) void bix_read_stream_kernel(const uint8_t* buf,
+                                                                           int64_t nchunks,
+                                                                           uint32_t* sink) {
+  constexpr int LOADS = kStreamChunk / 1024;  // 1 KiB direct loads per chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStreamWaves][kStreamRing * kStreamChunk];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t NW = (int64_t)gridDim.x * kStreamWaves;
+  const int64_t w = (int64_t)blockIdx.x * kStreamWaves + wave;
+  const int64_t mine = w < nchunks ? (nchunks - w + NW - 1) / NW : 0;  // chunks of this wave
+  const uint32_t base = (uint32_t)(uintptr_t)ring[wave];
+  auto issue = [&](int64_t i) {  // the wave's i-th chunk into slot i mod RING
+    const uint8_t* src = buf + (w + i * NW) * kStreamChunk;
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n)
+      lds_dma16_sv(src + n * 1024, (uint32_t)lane * 16,
+                   base + (uint32_t)((i % kStreamRing) * kStreamChunk + n * 1024));
+  };
+  for (int64_t i = 0; i < kStreamRing - 1 && i < mine; ++i) issue(i);
+  uint32_t acc = 0;
+  for (int64_t i = 0; i < mine; ++i) {
+    // chunk i has landed once at most the younger in-flight chunks remain
+    if (i + kStreamRing - 1 <= mine) wait_vmcnt_le<(kStreamRing - 2) * LOADS>();
+    else wait_vmcnt_le<0>();
+    acc ^= *(const uint32_t*)(ring[wave] + (i % kStreamRing) * kStreamChunk + lane * 16);
+    lds_reads_done();  // slot (i-1) mod RING is refilled next: its read is complete
+    if (i + kStreamRing - 1 < mine) issue(i + kStreamRing - 1);
   }
-  for (; i < n16; i += stride) acc ^= p[i];
-  const uint32_t t = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-  if (t == 0x9E3779B9u && acc[0] == 0x7F4A7C15u) sink[0] = t;
+  wait_vmcnt_le<0>();
+  if (acc == 0x9E3779B9u && lane == 63) sink[0] = acc;
 }
 
 }  // namespace
 
 hipError_t launch_read_stream(const void* p, int64_t bytes, int workgroups, uint32_t* sink,
                               hipStream_t st) {
-  hipLaunchKernelGGL(bix_read_stream_kernel, dim3((unsigned)workgroups), dim3(256), 0, st,
-                     (const u32x4*)p, bytes / 16, sink);
+  hipLaunchKernelGGL(bix_read_stream_kernel, dim3((unsigned)workgroups), dim3(64 * kStreamWaves),
+                     0, st, (const uint8_t*)p, bytes / kStreamChunk, sink);
   return hipGetLastError();
 }
 

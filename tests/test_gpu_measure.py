@@ -9,22 +9,22 @@ pytestmark = pytest.mark.gpu
 
 
 def test_read_stream_reads_and_writes_nothing():
-    x = torch.arange(1 << 18, dtype=torch.int32, device="cuda")   # 1 MiB
+    x = torch.arange(1 << 18, dtype=torch.int32, device="cuda")   # 1 MiB = 128 chunks
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-    for wg in (1, 7, 256, 2048):
+    for wg in (1, 7, 64, 256, 2048):
         assert bi.bix_read_stream(x, wg, sink) == 1 << 20
-    # a tail shorter than one grid stride and a tensor smaller than one stride
-    assert bi.bix_read_stream(x[:1000 * 4], 2048, sink) == 16000
+    # fewer chunks than a wave's ring, and fewer than waves
+    assert bi.bix_read_stream(x[:3 * 2048], 1, sink) == 3 * 8192
+    assert bi.bix_read_stream(x[:3 * 2048], 256, sink) == 3 * 8192
     torch.cuda.synchronize()
     assert sink.tolist() == [0, 0, 0, 0]
 
 
 def test_read_stream_rejects_ragged_sizes():
-    x = torch.zeros(5, dtype=torch.int32, device="cuda")   # 20 bytes
-    with pytest.raises(bi.BIError):
-        bi.bix_read_stream(x, 1)
-    with pytest.raises(bi.BIError):
-        bi.bix_read_stream(torch.zeros(8, dtype=torch.int32, device="cuda")[1:5], 1)
+    with pytest.raises(bi.BIError):   # 16000 bytes: not whole 8 KiB chunks
+        bi.bix_read_stream(torch.zeros(4000, dtype=torch.int32, device="cuda"), 1)
+    with pytest.raises(bi.BIError):   # misaligned
+        bi.bix_read_stream(torch.zeros(2049 * 4, dtype=torch.int32, device="cuda")[1:2049], 1)
 
 
 def test_mfma_loop_runs_and_writes_nothing():
