@@ -731,8 +731,9 @@ def e2e_llama8b(steps: int = 128):
     done with the non-invariant comparator kernels.  ``unique_outputs`` counts
     the distinct token sequences the probe gets over batches of 1, 4, 16 and 64
     (the news.hada.io page's GPT-4 experiment counted unique outputs over
-    repeated calls).  Wall times include Python's launch overhead (about 400 library
-    calls per forward)."""
+    repeated calls).  Decode steps are replayed from a captured HIP graph (about
+    400 library calls per step); the prefill calls are eager.  Wall times
+    include the prefill and the host's per-step bookkeeping."""
     import torch
     import synth
     from invariant_bi_matmul_amd.model import Decoder, LlamaConfig

@@ -35,7 +35,7 @@ from . import (PAGE, add, argmax, attn_decode, attn_prefill, attn_workspace_byte
                bix_attn_decode_splitkv, bix_matmul_splitk, bix_rmsnorm_splitrow, embed,
                make_shape, matmul, rmsnorm, rope, swiglu)
 
-__all__ = ["LlamaConfig", "LAYER_WEIGHTS", "weight_shapes", "Decoder"]
+__all__ = ["LlamaConfig", "LAYER_WEIGHTS", "weight_shapes", "Decoder", "DecodeGraph"]
 
 
 @dataclass(frozen=True)
@@ -166,12 +166,28 @@ class Decoder:
         bt = torch.tensor(table, **i32)
         last = torch.tensor([c - 1 for c in cu[1:]], **i32)
         decode = max(n_new) == 1
+        ws = self._decode_workspace(B, maxp, max(after)) if decode else None
+        logits, nxt = self._body(ids, pos, cu_q, kv_len, bt, last, max(n_new), max(after), ws)
+        for s, L in zip(seqs, after):
+            s.length = L
+        return logits, nxt
+
+    def _decode_workspace(self, B: int, maxp: int, max_len: int):
+        if self.comparator:
+            return None
+        cfg = self.cfg
+        shape = make_shape(B, cfg.n_q, cfg.n_kv, cfg.head_dim, maxp, self.num_pages, self.scale)
+        need = attn_workspace_bytes(shape, B, max_len)
+        return torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=self.device)
+
+    def _body(self, ids, pos, cu_q, kv_len, bt, last, max_new: int, max_len: int, ws):
+        """The stack on device tensors: T = len(ids) tokens of B = len(kv_len)
+        sequences; a decode step when max_new == 1.  Only device work, so a
+        decode step can be captured into a graph and replayed."""
+        cfg = self.cfg
+        T = ids.shape[0]
+        decode = max_new == 1
         nq, nkv, d = cfg.n_q, cfg.n_kv, cfg.head_dim
-        ws = None
-        if decode and not self.comparator:
-            shape = make_shape(B, nq, nkv, d, maxp, self.num_pages, self.scale)
-            need = attn_workspace_bytes(shape, B, max(after))
-            ws = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=dev)
         norm, mm = self._norm, self._mm
 
         x = embed(ids, self.w["embed"])
@@ -183,13 +199,13 @@ class Decoder:
             rope(q, k, pos, cfg.rope_theta)
             if decode and self.comparator:
                 o = bix_attn_decode_splitkv(q, k, v, kv_len, bt, self.kc[li], self.vc[li],
-                                            self.scale, max(after))
+                                            self.scale, max_len)
             elif decode:
                 o = attn_decode(q, k, v, kv_len, bt, self.kc[li], self.vc[li], self.scale,
-                                max(after), workspace=ws)
+                                max_len, workspace=ws)
             else:
                 o = attn_prefill(q, k, v, cu_q, kv_len, bt, self.kc[li], self.vc[li], self.scale,
-                                 max(n_new))
+                                 max_new)
             add(x, mm(o.view(T, nq * d), lw["wo"]), out=x)
             h = norm(x, lw["mlp_norm"])
             g = mm(h, lw["w_gate"])
@@ -197,16 +213,21 @@ class Decoder:
             add(x, mm(g, lw["w_down"]), out=x)
         xl = embed(last, x)  # the last new token of each sequence (a row gather)
         logits = mm(norm(xl, self.w["final_norm"]), self.w["lm_head"], out_dtype=torch.float32)
-        nxt = argmax(logits)
-        for s, L in zip(seqs, after):
-            s.length = L
-        return logits, nxt
+        return logits, argmax(logits)
+
+    def decode_graph(self, sids: Sequence[int], max_len: int) -> "DecodeGraph":
+        """Decode steps of the sequences ``sids`` (in this order) until any
+        reaches ``max_len`` positions, replayed from one captured graph."""
+        return DecodeGraph(self, list(sids), max_len)
 
     # ---- greedy generation -----------------------------------------------------
     def generate(self, prompts: Dict[int, Sequence[int]], steps: int,
-                 chunk: Optional[int] = None, keep_logits: Sequence[int] = ()):
+                 chunk: Optional[int] = None, keep_logits: Sequence[int] = (),
+                 graph: bool = True):
         """Prefill every prompt (in one call, or in calls of ``chunk`` tokens per
-        sequence), then ``steps`` greedy decode steps over all of them.
+        sequence), then ``steps`` greedy decode steps over all of them (with
+        ``graph``, replayed from a captured graph: the same kernels on the
+        same inputs, so the same bits).
         Returns ({id: generated tokens}, {id: [fp32 logits per generated token]})
         where logits are kept (on the device) only for ids in ``keep_logits``."""
         for sid in prompts:
@@ -232,8 +253,14 @@ class Decoder:
                     toks[sid].append(nxt[i])
                     if sid in kept:
                         kept[sid].append(logits[i].clone())
+        dg = None
+        if graph and steps > 2:
+            dg = self.decode_graph(sids, max(self.seqs[sid].length for sid in sids) + steps)
         for _ in range(steps - 1):
-            logits, nxt = self.forward([(sid, [toks[sid][-1]]) for sid in sids])
+            if dg is not None:
+                logits, nxt = dg.step([toks[sid][-1] for sid in sids])
+            else:
+                logits, nxt = self.forward([(sid, [toks[sid][-1]]) for sid in sids])
             nxt = nxt.tolist()
             for i, sid in enumerate(sids):
                 toks[sid].append(nxt[i])
@@ -242,3 +269,69 @@ class Decoder:
         for sid in sids:
             self.release(sid)
         return toks, kept
+
+
+class DecodeGraph:
+    """One decode step of a fixed list of sequences, captured into a HIP graph
+    on first use and replayed for every later step.  A step of the stack is
+    about a dozen launches per layer; replayed, they leave the host at once.
+
+    The step's index arrays (token ids, positions, kv_len, block table) live
+    in static device buffers that each step overwrites before the replay.
+    The attention launch is sized for ``max_len`` positions; its kernels read
+    the actual lengths from kv_len, so a step's arithmetic is that of an
+    eager ``Decoder.forward`` on the same inputs.  Outputs (logits, next
+    tokens) are static tensors, valid until the next step."""
+
+    def __init__(self, dec: Decoder, sids: List[int], max_len: int):
+        self.dec, self.sids = dec, sids
+        B = len(sids)
+        self.maxp = (max_len + PAGE - 1) // PAGE
+        self.max_len = self.maxp * PAGE
+        i32 = dict(dtype=torch.int32, device=dec.device)
+        self.ids = torch.zeros(B, **i32)
+        self.pos = torch.zeros(B, **i32)
+        self.kv_len = torch.ones(B, **i32)
+        self.bt = torch.zeros(B, self.maxp, **i32)
+        self.cu = torch.arange(B + 1, **i32)
+        self.last = torch.arange(B, **i32)
+        self.ws = dec._decode_workspace(B, self.maxp, self.max_len)
+        self.graph = None
+        self.out = None
+
+    def _run(self):
+        return self.dec._body(self.ids, self.pos, self.cu, self.kv_len, self.bt, self.last, 1,
+                              self.max_len, self.ws)
+
+    def step(self, tokens: Sequence[int]):
+        dec, B = self.dec, len(self.sids)
+        seqs = [dec.seqs[sid] for sid in self.sids]
+        if len(tokens) != B:
+            raise ValueError("one token per sequence")
+        for s in seqs:
+            if s.length + 1 > self.max_len:
+                raise RuntimeError("sequence longer than the captured step allows")
+            dec._reserve(s, s.length + 1)
+        rows = [s.pages + [s.pages[-1]] * (self.maxp - len(s.pages)) for s in seqs]
+        flat = (list(tokens) + [s.length for s in seqs] + [s.length + 1 for s in seqs]
+                + [p for r in rows for p in r])
+        dev = torch.tensor(flat, dtype=torch.int32, device=dec.device)  # one host-to-device copy
+        self.ids.copy_(dev[:B])
+        self.pos.copy_(dev[B:2 * B])
+        self.kv_len.copy_(dev[2 * B:3 * B])
+        self.bt.copy_(dev[3 * B:].view(B, self.maxp))
+        if self.graph is None:
+            # warm up once outside the capture (the step's K/V append is
+            # idempotent: the replay writes the same values to the same slots)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self._run()
+            torch.cuda.current_stream().wait_stream(side)
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph):
+                self.out = self._run()
+        self.graph.replay()
+        for s in seqs:
+            s.length += 1
+        return self.out

@@ -118,6 +118,22 @@ def test_toy_stack_alone_batched_and_chunked_are_bitwise_equal():
     assert _same(alone[1][0], together[1][0]) and _same(alone[1][0], chunked[1][0])
 
 
+@pytest.mark.parametrize("comparator", [False, True])
+def test_graph_decode_equals_eager(comparator):
+    """Decode steps replayed from a captured graph give the eager steps' tokens
+    and logits bit for bit (the comparator too: its splits follow the batch,
+    which a graph keeps fixed)."""
+    w = _weights(TOY, seed=2)
+    batch = {5: synth.token_ids(40, TOY.vocab, 2, "g.a"),
+             1: synth.token_ids(270, TOY.vocab, 2, "g.b"),
+             8: synth.token_ids(3, TOY.vocab, 2, "g.c")}
+    runs = [Decoder(TOY, w, max_tokens=4096, comparator=comparator).generate(
+        batch, 20, keep_logits=[5, 1, 8], graph=g) for g in (False, True)]
+    for sid in batch:
+        assert runs[0][0][sid] == runs[1][0][sid], sid
+        assert _same(runs[0][1][sid], runs[1][1][sid]), sid
+
+
 def test_stack_logits_follow_the_argmax_rule():
     w = _weights(TOY, seed=1)
     toks, logits = Decoder(TOY, w, max_tokens=1024).generate(
