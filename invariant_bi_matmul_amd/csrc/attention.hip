@@ -370,7 +370,7 @@ __device__ __forceinline__ void unpack_i16x8(u32x4 raw, bf16x8& hi, bf16x8& lo) 
 // LDS operand reads are issued this many MFMA operands ahead of their use, so
 // their latency hides behind the MFMAs in between (one wave per SIMD: nothing
 // else would hide it).
-constexpr int kOperandsAhead = 4;
+constexpr int kOperandsAhead = 6;
 
 // Whether an operand source reads the int16 cache (Src::Q16, default false).
 template <class S, class = void>
