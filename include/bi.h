@@ -260,6 +260,23 @@ int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, i
  * gate, up, out bf16 [n], n % 8 == 0; out may alias gate or up. */
 int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream);
 
+/* The output of one fused q|k|v projection split into the q, k and v tensors
+ * the attention calls take, with bi_rope's rotation (the same arithmetic)
+ * applied to the q and k heads.  qkv bf16 [tokens, n_q + 2 n_kv, head_dim]
+ * (row t: t's q heads, then k heads, then v heads); q bf16 [tokens, n_q,
+ * head_dim], k and v bf16 [tokens, n_kv, head_dim], none overlapping qkv;
+ * pos int32 [tokens].  head_dim even and <= 256; theta > 1.  A fused
+ * projection (one bi_matmul against [W_q | W_k | W_v]) gives every column the
+ * bits of the separate ones: a column's dot product does not depend on its
+ * neighbours. */
+int bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, int64_t tokens,
+                int32_t n_q, int32_t n_kv, int32_t head_dim, float theta, void* stream);
+
+/* bi_swiglu over the output of one fused gate|up projection: gu bf16
+ * [rows, 2f] (row r: gate, then up), out bf16 [rows, f] not overlapping gu;
+ * f % 8 == 0. */
+int bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* stream);
+
 /* out = bf16(a + b) element-wise (the residual add).  bf16 [n], n % 8 == 0;
  * out may alias a or b. */
 int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);

@@ -22,6 +22,7 @@ __all__ = [
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
+    "qkv_rope", "swiglu_pair",
     "attn_prefill_i16", "attn_decode_i16", "bix_mfma_loop",
     "bix_read_stream",
 ]
@@ -98,6 +99,8 @@ def load_library(path: str):
         "bi_embed": (ctypes.c_int, [P, P, P, i64, i64, i64, P]),
         "bi_rope": (ctypes.c_int, [P, P, P, i64, i32, i32, i32, f32, P]),
         "bi_swiglu": (ctypes.c_int, [P, P, P, i64, P]),
+        "bi_qkv_rope": (ctypes.c_int, [P, P, P, P, P, i64, i32, i32, i32, f32, P]),
+        "bi_swiglu_pair": (ctypes.c_int, [P, P, i64, i64, P]),
         "bi_add": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_argmax": (ctypes.c_int, [P, P, i64, i64, P]),
         "bix_mfma_loop": (ctypes.c_int, [i64, i32, P, P]),
@@ -378,6 +381,39 @@ def swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor] = N
     _dev(up, "up", torch.bfloat16, gate.shape)
     o = torch.empty_like(gate) if out is None else _dev(out, "out", torch.bfloat16, gate.shape)
     _check("bi_swiglu", load().bi_swiglu(_ptr(gate), _ptr(up), _ptr(o), gate.numel(), _stream()))
+    return o
+
+
+def qkv_rope(qkv: torch.Tensor, pos: torch.Tensor, n_q: int, n_kv: int, theta: float,
+             q: Optional[torch.Tensor] = None, k: Optional[torch.Tensor] = None,
+             v: Optional[torch.Tensor] = None):
+    """Split a fused q|k|v projection output qkv bf16 [T, (n_q + 2 n_kv) * d]
+    into q [T, n_q, d], k and v [T, n_kv, d], rotating q and k as ``rope``
+    does.  Returns (q, k, v)."""
+    _dev(qkv, "qkv", torch.bfloat16)
+    if qkv.dim() != 2 or qkv.shape[1] % (n_q + 2 * n_kv) != 0:
+        raise ValueError("need qkv [T, (n_q + 2 n_kv) * d]")
+    T = qkv.shape[0]
+    d = qkv.shape[1] // (n_q + 2 * n_kv)
+    _dev(pos, "pos", torch.int32, (T,))
+    new = lambda t, h, name: (torch.empty(T, h, d, dtype=torch.bfloat16, device=qkv.device)
+                              if t is None else _dev(t, name, torch.bfloat16, (T, h, d)))
+    q, k, v = new(q, n_q, "q"), new(k, n_kv, "k"), new(v, n_kv, "v")
+    _check("bi_qkv_rope", load().bi_qkv_rope(_ptr(qkv), _ptr(pos), _ptr(q), _ptr(k), _ptr(v), T,
+                                             n_q, n_kv, d, float(theta), _stream()))
+    return q, k, v
+
+
+def swiglu_pair(gu: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """``swiglu`` over a fused gate|up projection output gu bf16 [rows, 2f]
+    (gate columns first); returns bf16 [rows, f]."""
+    _dev(gu, "gu", torch.bfloat16)
+    if gu.dim() != 2 or gu.shape[1] % 2 != 0:
+        raise ValueError("need gu [rows, 2f]")
+    rows, f = gu.shape[0], gu.shape[1] // 2
+    o = (torch.empty(rows, f, dtype=torch.bfloat16, device=gu.device) if out is None
+         else _dev(out, "out", torch.bfloat16, (rows, f)))
+    _check("bi_swiglu_pair", load().bi_swiglu_pair(_ptr(gu), _ptr(o), rows, f, _stream()))
     return o
 
 

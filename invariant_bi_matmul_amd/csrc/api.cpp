@@ -367,6 +367,36 @@ int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, i
   }
 }
 
+int bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, int64_t tokens,
+                int32_t n_q, int32_t n_kv, int32_t head_dim, float theta, void* stream) {
+  try {
+    if (tokens < 0 || n_q <= 0 || n_kv <= 0) return BI_ERR_INVALID_SHAPE;
+    if (tokens == 0) return BI_OK;
+    if (head_dim <= 0 || head_dim % 2 != 0 || head_dim > 256) return BI_ERR_INVALID_SHAPE;
+    if (!(theta > 1.0f) || !isfinite(theta)) return BI_ERR_INVALID_SHAPE;
+    if (tokens > kMaxGridX || (int64_t)n_q + 2 * (int64_t)n_kv > kMaxGridYZ)
+      return BI_ERR_UNSUPPORTED;
+    if (!qkv || !pos || !q || !k || !v) return BI_ERR_NULL_POINTER;
+    if (!aligned4(pos)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_qkv_rope(qkv, pos, q, k, v, tokens, n_q, n_kv, head_dim, theta,
+                                          (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+int bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* stream) {
+  try {
+    if (rows < 0 || f < 0 || f % 8 != 0) return BI_ERR_INVALID_SHAPE;
+    if (rows == 0 || f == 0) return BI_OK;
+    if (gu == nullptr || out == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(gu) || !aligned16(out)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_swiglu_pair(gu, out, rows, f, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
 int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream) {
   try {
     if (n < 0 || n % 8 != 0) return BI_ERR_INVALID_SHAPE;

@@ -73,6 +73,9 @@ hipError_t launch_embed(const int32_t* ids, const void* table, void* out, int64_
                         int64_t hidden, int64_t vocab, hipStream_t st);
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int nq, int nkv,
                        int d, float theta, hipStream_t st);
+hipError_t launch_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v,
+                           int64_t tokens, int nq, int nkv, int d, float theta, hipStream_t st);
+hipError_t launch_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, hipStream_t st);
 hipError_t launch_swiglu(const void* gate, const void* up, void* out, int64_t n, hipStream_t st);
 hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStream_t st);
 hipError_t launch_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, hipStream_t st);

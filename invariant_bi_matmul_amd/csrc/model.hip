@@ -40,48 +40,90 @@ __global__ __launch_bounds__(kElemThreads) void embed_kernel(const int32_t* __re
 // p and i < d/2, with a = x[i], b = x[i + d/2] and angle = p * theta^(-2i/d):
 //   x[i] = a cos - b sin,  x[i + d/2] = a sin + b cos.
 // Grid (tokens, n_q + n_kv); thread i owns pair i.  In place.
+// Pair i of one head row: src[i], src[i + d/2] rotated by the angle of
+// position p, written to dst (which may be src).
+__device__ __forceinline__ void rope_pair(const uint16_t* src, uint16_t* dst, int i, int d, int p,
+                                          float theta) {
+  const int half = d / 2;
+  const float inv_freq = powf(theta, -(float)(2 * i) / (float)d);
+  const float angle = (float)p * inv_freq;
+  const float s = sinf(angle), c = cosf(angle);
+  const float a = bf16_to_f32(src[i]), b = bf16_to_f32(src[i + half]);
+  const float ya = a * c - b * s;
+  const float yb = a * s + b * c;
+  dst[i] = (uint16_t)f32_to_bf16(ya);
+  dst[i + half] = (uint16_t)f32_to_bf16(yb);
+}
+
 __global__ void rope_kernel(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
                             const int32_t* __restrict__ pos, int nq, int nkv, int d,
                             float theta) {
   const int64_t t = blockIdx.x;
   const int h = blockIdx.y;
   const int i = threadIdx.x;
-  const int half = d / 2;
-  if (i >= half) return;
+  if (i >= d / 2) return;
   uint16_t* x = h < nq ? q + (t * nq + h) * d : k + (t * nkv + (h - nq)) * d;
-  const float inv_freq = powf(theta, -(float)(2 * i) / (float)d);
-  const float angle = (float)pos[t] * inv_freq;
-  const float s = sinf(angle), c = cosf(angle);
-  const float a = bf16_to_f32(x[i]), b = bf16_to_f32(x[i + half]);
-  const float ya = a * c - b * s;
-  const float yb = a * s + b * c;
-  x[i] = (uint16_t)f32_to_bf16(ya);
-  x[i + half] = (uint16_t)f32_to_bf16(yb);
+  rope_pair(x, x, i, d, pos[t], theta);
+}
+
+// The output row of a fused q|k|v projection ([nq + 2 nkv] heads of d) split
+// into contiguous q, k and v, with the rotary embedding of rope_kernel applied
+// to the q and k heads on the way (the same arithmetic).
+__global__ void qkv_rope_kernel(const uint16_t* __restrict__ qkv, const int32_t* __restrict__ pos,
+                                uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                uint16_t* __restrict__ v, int nq, int nkv, int d, float theta) {
+  const int64_t t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int i = threadIdx.x;
+  if (i >= d / 2) return;
+  const uint16_t* src = qkv + (t * (nq + 2 * nkv) + h) * d;
+  if (h < nq + nkv) {
+    uint16_t* dst = h < nq ? q + (t * nq + h) * d : k + (t * nkv + (h - nq)) * d;
+    rope_pair(src, dst, i, d, pos[t], theta);
+  } else {
+    uint16_t* dst = v + (t * nkv + (h - nq - nkv)) * d;
+    dst[i] = src[i];
+    dst[i + d / 2] = src[i + d / 2];
+  }
 }
 
 // out = bf16(silu(gate) * up), silu(g) = g / (1 + e^-g); eight elements per
 // thread.
+__device__ __forceinline__ u32x4 swiglu8(u32x4 g, u32x4 u) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float gv = h ? bf16_hi(g[j]) : bf16_lo(g[j]);
+      const float uv = h ? bf16_hi(u[j]) : bf16_lo(u[j]);
+      const float silu = gv / (1.0f + expf(-gv));
+      r[h] = silu * uv;
+    }
+    o[j] = pack_bf16x2(r[0], r[1]);
+  }
+  return o;
+}
+
 __global__ __launch_bounds__(kElemThreads) void swiglu_kernel(const u32x4* __restrict__ gate,
                                                               const u32x4* __restrict__ up,
                                                               u32x4* __restrict__ out,
                                                               int64_t vecs) {
   for (int64_t v = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; v < vecs;
+       v += (int64_t)gridDim.x * kElemThreads)
+    out[v] = swiglu8(gate[v], up[v]);
+}
+
+// The same over the output of a fused gate|up projection: row r of gu holds
+// gate (f values) then up (f values); out is [rows, f].  fv = f / 8.
+__global__ __launch_bounds__(kElemThreads) void swiglu_pair_kernel(const u32x4* __restrict__ gu,
+                                                                   u32x4* __restrict__ out,
+                                                                   int64_t vecs, int64_t fv) {
+  for (int64_t v = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; v < vecs;
        v += (int64_t)gridDim.x * kElemThreads) {
-    const u32x4 g = gate[v], u = up[v];
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float r[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float gv = h ? bf16_hi(g[j]) : bf16_lo(g[j]);
-        const float uv = h ? bf16_hi(u[j]) : bf16_lo(u[j]);
-        const float silu = gv / (1.0f + expf(-gv));
-        r[h] = silu * uv;
-      }
-      o[j] = pack_bf16x2(r[0], r[1]);
-    }
-    out[v] = o;
+    const int64_t r = v / fv, c = v - r * fv;
+    out[v] = swiglu8(gu[r * 2 * fv + c], gu[r * 2 * fv + fv + c]);
   }
 }
 
@@ -191,6 +233,22 @@ hipError_t launch_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int
   const int threads = ((d / 2 + kWave - 1) / kWave) * kWave;
   hipLaunchKernelGGL(rope_kernel, dim3((unsigned)tokens, (unsigned)(nq + nkv)), dim3(threads), 0,
                      st, (uint16_t*)q, (uint16_t*)k, pos, nq, nkv, d, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v,
+                           int64_t tokens, int nq, int nkv, int d, float theta, hipStream_t st) {
+  const int threads = ((d / 2 + kWave - 1) / kWave) * kWave;
+  hipLaunchKernelGGL(qkv_rope_kernel, dim3((unsigned)tokens, (unsigned)(nq + 2 * nkv)),
+                     dim3(threads), 0, st, (const uint16_t*)qkv, pos, (uint16_t*)q, (uint16_t*)k,
+                     (uint16_t*)v, nq, nkv, d, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, hipStream_t st) {
+  const int64_t vecs = rows * f / 8;
+  hipLaunchKernelGGL(swiglu_pair_kernel, dim3(elem_grid(vecs)), dim3(kElemThreads), 0, st,
+                     (const u32x4*)gu, (u32x4*)out, vecs, f / 8);
   return hipGetLastError();
 }
 

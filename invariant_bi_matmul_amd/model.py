@@ -3,11 +3,13 @@
 Every arithmetic step is a libbi call:
 - token embedding and row gathers: ``bi_embed``;
 - ``bi_rmsnorm``, then ``bi_matmul`` for the q/k/v, output, gate/up/down and
-  lm_head projections;
-- ``bi_rope``;
+  lm_head projections (q|k|v and gate|up as one matmul each by default);
+- ``bi_qkv_rope`` (split of the fused q|k|v output plus rotary embedding), or
+  ``bi_rope``;
 - ``bi_attn_prefill`` / ``bi_attn_decode`` over a paged KV cache (16-token
   pages, fixed 256-position splits, fixed-order combine);
-- ``bi_add`` (residual), ``bi_swiglu``, and ``bi_argmax`` (greedy sampling).
+- ``bi_add`` (residual), ``bi_swiglu_pair`` / ``bi_swiglu``, and ``bi_argmax``
+  (greedy sampling).
 
 This module keeps only bookkeeping: the weights, the KV pages each sequence
 owns, and the per-call index arrays (token ids, positions, cu_q, kv_len,
@@ -33,7 +35,7 @@ import torch
 
 from . import (PAGE, add, argmax, attn_decode, attn_prefill, attn_workspace_bytes,
                bix_attn_decode_splitkv, bix_matmul_splitk, bix_rmsnorm_splitrow, embed,
-               make_shape, matmul, rmsnorm, rope, swiglu)
+               make_shape, matmul, qkv_rope, rmsnorm, rope, swiglu, swiglu_pair)
 
 __all__ = ["LlamaConfig", "LAYER_WEIGHTS", "weight_shapes", "Decoder", "DecodeGraph"]
 
@@ -80,10 +82,18 @@ class Decoder:
     ``comparator=True`` swaps in the library's non-invariant comparators
     (split-row RMSNorm, split-K matmul and split-KV decode attention, whose
     split counts follow the batch size), as a negative control: with them a
-    sequence's bits depend on its companions."""
+    sequence's bits depend on its companions.
+
+    ``fuse=True`` runs the q, k and v projections as one matmul against
+    [W_q | W_k | W_v] (then ``bi_qkv_rope`` splits and rotates), and gate and
+    up as one against [W_gate | W_up] (then ``bi_swiglu_pair``): one launch
+    fills the GPU where three small ones each left most of it idle.  Every
+    output column is the same dot product in the same k order either way, so
+    the bits are those of the separate projections."""
 
     def __init__(self, cfg: LlamaConfig, weights: dict, max_tokens: int,
-                 device: Optional[torch.device] = None, comparator: bool = False):
+                 device: Optional[torch.device] = None, comparator: bool = False,
+                 fuse: bool = True):
         glob, layer = weight_shapes(cfg)
         for name, shape in glob.items():
             if tuple(weights[name].shape) != shape or weights[name].dtype != torch.bfloat16:
@@ -97,6 +107,11 @@ class Decoder:
         self.cfg = cfg
         self.w = weights
         self.device = device or weights["embed"].device
+        self.fuse = fuse
+        # concatenated projection weights (a one-off copy when the model loads)
+        self.fused = [{"w_qkv": torch.cat([lw["wq"], lw["wk"], lw["wv"]], dim=1).contiguous(),
+                       "w_gu": torch.cat([lw["w_gate"], lw["w_up"]], dim=1).contiguous()}
+                      for lw in weights["layers"]] if fuse else None
         self.num_pages = (max_tokens + PAGE - 1) // PAGE + 1
         cache = (self.num_pages, cfg.n_kv, PAGE, cfg.head_dim)
         self.kc = [torch.zeros(cache, dtype=torch.bfloat16, device=self.device)
@@ -193,10 +208,13 @@ class Decoder:
         x = embed(ids, self.w["embed"])
         for li, lw in enumerate(self.w["layers"]):
             h = norm(x, lw["attn_norm"])
-            q = mm(h, lw["wq"]).view(T, nq, d)
-            k = mm(h, lw["wk"]).view(T, nkv, d)
-            v = mm(h, lw["wv"]).view(T, nkv, d)
-            rope(q, k, pos, cfg.rope_theta)
+            if self.fuse:
+                q, k, v = qkv_rope(mm(h, self.fused[li]["w_qkv"]), pos, nq, nkv, cfg.rope_theta)
+            else:
+                q = mm(h, lw["wq"]).view(T, nq, d)
+                k = mm(h, lw["wk"]).view(T, nkv, d)
+                v = mm(h, lw["wv"]).view(T, nkv, d)
+                rope(q, k, pos, cfg.rope_theta)
             if decode and self.comparator:
                 o = bix_attn_decode_splitkv(q, k, v, kv_len, bt, self.kc[li], self.vc[li],
                                             self.scale, max_len)
@@ -208,8 +226,11 @@ class Decoder:
                                  max_new)
             add(x, mm(o.view(T, nq * d), lw["wo"]), out=x)
             h = norm(x, lw["mlp_norm"])
-            g = mm(h, lw["w_gate"])
-            swiglu(g, mm(h, lw["w_up"]), out=g)
+            if self.fuse:
+                g = swiglu_pair(mm(h, self.fused[li]["w_gu"]))
+            else:
+                g = mm(h, lw["w_gate"])
+                swiglu(g, mm(h, lw["w_up"]), out=g)
             add(x, mm(g, lw["w_down"]), out=x)
         xl = embed(last, x)  # the last new token of each sequence (a row gather)
         logits = mm(norm(xl, self.w["final_norm"]), self.w["lm_head"], out_dtype=torch.float32)

@@ -134,6 +134,38 @@ def test_graph_decode_equals_eager(comparator):
         assert _same(runs[0][1][sid], runs[1][1][sid]), sid
 
 
+def test_fused_projections_equal_separate_ones():
+    """q|k|v and gate|up as one matmul each (then bi_qkv_rope and
+    bi_swiglu_pair) give the separate projections' tokens and logits bit for
+    bit, in prefill and decode."""
+    w = _weights(TOY, seed=3)
+    batch = {2: synth.token_ids(70, TOY.vocab, 3, "f.a"),
+             4: synth.token_ids(300, TOY.vocab, 3, "f.b")}
+    runs = [Decoder(TOY, w, max_tokens=4096, fuse=f).generate(batch, 6, chunk=64,
+                                                              keep_logits=[2, 4])
+            for f in (False, True)]
+    for sid in batch:
+        assert runs[0][0][sid] == runs[1][0][sid], sid
+        assert _same(runs[0][1][sid], runs[1][1][sid]), sid
+
+
+def test_qkv_rope_and_swiglu_pair_match_the_separate_kernels():
+    T, nq, nkv, d = 37, 8, 2, 64
+    qkv = synth.device_normal_bf16((T, (nq + 2 * nkv) * d), 0.0, 2.0, 4, "f.qkv", dev())
+    pos = torch.arange(1000, 1000 + T, dtype=torch.int32, device=dev())
+    q, k, v = bi.qkv_rope(qkv, pos, nq, nkv, 500000.0)
+    rows = qkv.view(T, nq + 2 * nkv, d)
+    q2, k2 = rows[:, :nq].contiguous(), rows[:, nq:nq + nkv].contiguous()
+    bi.rope(q2, k2, pos, 500000.0)
+    assert torch.equal(q.view(torch.int16), q2.view(torch.int16))
+    assert torch.equal(k.view(torch.int16), k2.view(torch.int16))
+    assert torch.equal(v.view(torch.int16), rows[:, nq + nkv:].contiguous().view(torch.int16))
+    gu = synth.device_normal_bf16((T, 2 * 512), 0.0, 3.0, 4, "f.gu", dev())
+    got = bi.swiglu_pair(gu)
+    want = bi.swiglu(gu[:, :512].contiguous(), gu[:, 512:].contiguous())
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
 def test_stack_logits_follow_the_argmax_rule():
     w = _weights(TOY, seed=1)
     toks, logits = Decoder(TOY, w, max_tokens=1024).generate(
