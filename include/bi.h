@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BI_ABI_VERSION 1
+#define BI_ABI_VERSION 2
 
 typedef enum {
   BI_OK = 0,
@@ -313,13 +313,15 @@ int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new
                         float* v_scale, void* out, float* lse, int64_t total_q,
                         int32_t max_q_per_seq, void* stream);
 
-/* Decode over the int16 cache: one new token per sequence (q, k_new, v_new
- * [B, ...] as in bi_attn_decode), appended, then attended by the prefill
- * kernel (one workgroup per sequence and kv head walks the splits in order
- * and folds them in registers).  No workspace. */
+/* Decode over the int16 cache, as bi_attn_decode: one new token per sequence
+ * (q, k_new, v_new [B, ...]), quantised and appended, then the split
+ * partials (the decode kernel, each unit's 256 key and value factors staged
+ * with its q) and the fixed-order fold.  max_kv_len, workspace and
+ * workspace_bytes as in bi_attn_decode (bi_attn_workspace_bytes sizes it). */
 int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                        const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                        void* v_cache, float* k_scale, float* v_scale, void* out, float* lse,
+                       int32_t max_kv_len, void* workspace, size_t workspace_bytes,
                        void* stream);
 
 /* ---- Error-compensated matmul ---------------------------------------------

@@ -107,7 +107,8 @@ def load_library(path: str):
         "bix_read_stream": (ctypes.c_int, [P, i64, i32, P, P]),
         "bi_attn_prefill_i16": (ctypes.c_int,
                                 [SP, P, P, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
-        "bi_attn_decode_i16": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "bi_attn_decode_i16": (ctypes.c_int,
+                               [SP, P, P, P, P, P, P, P, P, P, P, P, i32, P, sz, P]),
         "bi_matmul_ec_pack_w": (ctypes.c_int, [P, P, i64, i64, P]),
         "bi_matmul_ec_workspace_bytes": (sz, [i64, i64]),
         "bi_matmul_ec": (ctypes.c_int, [P, P, P, i64, i64, i64, P, sz, P]),
@@ -518,8 +519,11 @@ def attn_prefill_i16(q, k_new, v_new, cu_q, kv_len, block_table, k_cache, v_cach
 
 
 def attn_decode_i16(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, k_scale, v_scale,
-                    softmax_scale, out=None, lse=None, with_lse: bool = False):
-    """One new token per sequence over the int16 cache; q bf16 [B, n_q, d]."""
+                    softmax_scale, max_kv_len: Optional[int] = None, workspace=None, out=None,
+                    lse=None, with_lse: bool = False):
+    """One new token per sequence over the int16 cache; q bf16 [B, n_q, d].
+    ``max_kv_len`` (host) bounds every kv_len after the append; by default the
+    block table's capacity."""
     P, nkv, d = _i16_cache(k_cache, v_cache, k_scale, v_scale)
     _dev(q, "q", torch.bfloat16)
     B, nq, dq = q.shape
@@ -537,9 +541,15 @@ def attn_decode_i16(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, k_sc
     if lse is not None:
         _dev(lse, "lse", torch.float32, (B, nq))
     shape = make_shape(B, nq, nkv, d, block_table.shape[1], P, softmax_scale)
+    if max_kv_len is None:
+        max_kv_len = block_table.shape[1] * PAGE
+    need = attn_workspace_bytes(shape, B, max_kv_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=q.device)
     _check("bi_attn_decode_i16", load().bi_attn_decode_i16(
         ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_len), _ptr(block_table),
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(o), _ptr(lse),
+        int(max_kv_len), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream()))
     return (o, lse) if lse is not None else o
 

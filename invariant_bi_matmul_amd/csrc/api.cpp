@@ -488,28 +488,26 @@ int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new
 int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                        const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                        void* v_cache, float* k_scale, float* v_scale, void* out, float* lse,
+                       int32_t max_kv_len, void* workspace, size_t workspace_bytes,
                        void* stream) {
   try {
-    const int c = check_attn_shape(s);
+    const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
+                               max_kv_len, workspace);
+    if (c < 0) return BI_OK;
     if (c != BI_OK) return c;
-    if (s->num_seqs == 0) return BI_OK;
+    if (!k_scale || !v_scale) return BI_ERR_NULL_POINTER;
+    if (!aligned16(k_scale) || !aligned16(v_scale)) return BI_ERR_INVALID_SHAPE;
+    const int ns = (max_kv_len + bi::kSplit - 1) / bi::kSplit;
+    if (workspace_bytes < decode_ws_bytes(s, s->num_seqs, ns)) return BI_ERR_WORKSPACE_TOO_SMALL;
     if ((int64_t)s->num_seqs * s->num_kv_heads > kMaxGridX) return BI_ERR_UNSUPPORTED;
-    if (!q || !k_new || !v_new || !kv_len || !block_table || !k_cache || !v_cache || !k_scale ||
-        !v_scale || !out)
-      return BI_ERR_NULL_POINTER;
-    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(out) ||
-        !aligned4(lse) || !aligned4(kv_len) || !aligned4(block_table))
-      return BI_ERR_INVALID_SHAPE;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
-    BI_CHECK_TABLES(s, kv_len, nullptr, block_table, s->max_pages_per_seq * s->page_size, 1, 0,
-                    st);
+    BI_CHECK_TABLES(s, kv_len, nullptr, block_table, max_kv_len, 1, 0, st);
     hipError_t e = bi::launch_kv_append_i16(d, k_new, v_new, nullptr, kv_len, block_table,
                                             k_cache, v_cache, k_scale, v_scale, 1, st);
     if (e != hipSuccess) return BI_ERR_HIP;
-    return hip_status(bi::launch_attn_prefill(d, q, nullptr, kv_len, block_table, k_cache,
-                                              v_cache, out, lse, 1, st, k_scale, v_scale));
+    return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
+                                             ns, (float*)workspace, st, k_scale, v_scale));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }

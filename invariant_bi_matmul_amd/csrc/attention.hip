@@ -393,7 +393,7 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
   u32x4 buf[PD];
   // operand o = (chunk c, half h, d-step t); a chunk's first read waits for
   // (and lets the source refill around) that chunk
-  auto read = [&](auto oc) {
+  auto read = [&](auto oc) __attribute__((always_inline)) {
     constexpr int o = decltype(oc)::value;
     constexpr int c = o / OPC, h = (o % OPC) / DS, t = o % DS;
     if constexpr (o % OPC == 0) src.template step<c>();
@@ -401,7 +401,7 @@ __device__ __forceinline__ void split_qk(const Src& src, int key0, int key_end, 
   };
   static_for<0, PD>(read);
   f32x4 acc[NB][2];
-  static_for<0, NOP>([&](auto oc) {
+  static_for<0, NOP>([&](auto oc) __attribute__((always_inline)) {
     constexpr int o = decltype(oc)::value;
     constexpr int c = o / OPC, h = (o % OPC) / DS, t = o % DS;
     if constexpr (o % OPC == 0) {
@@ -511,14 +511,14 @@ __device__ __forceinline__ void split_pv(const Src& src, const u32x4 (&p)[NB][8]
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[b][i] = f32x4{};
   bf16x8 buf[PD];
-  auto read = [&](auto oc) {
+  auto read = [&](auto oc) __attribute__((always_inline)) {
     constexpr int op = decltype(oc)::value;
     constexpr int c = op / DB, i = op % DB;
     if constexpr (i == 0) src.template step<8 + c>();
     buf[op % PD] = src.template v<c>(i);
   };
   static_for<0, PD>(read);
-  static_for<0, NOP>([&](auto oc) {
+  static_for<0, NOP>([&](auto oc) __attribute__((always_inline)) {
     constexpr int op = decltype(oc)::value;
     constexpr int c = op / DB, i = op % DB;
     const bf16x8 va = buf[op % PD];
@@ -673,13 +673,15 @@ struct DecodeUnit {
   int g, b, s, key0, last;
 };
 
-template <int D, int RING_>
+template <int D, int RING_, bool Q16_ = false>
 struct StreamSrc {
+  static constexpr bool Q16 = Q16_;                  // int16 cache
   static constexpr int RING = RING_;
   static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
   static constexpr int LOADS = SLOT / 1024;          // 1 KiB loads per chunk
   static constexpr int AHEAD = RING - 1;             // chunks in flight
-  static constexpr int QLOADS = 16 * KV<D>::ROWB / 1024;  // q copy of the next unit
+  // q copy of the next unit (and, int16 cache, its key and value factors)
+  static constexpr int QLOADS = 16 * KV<D>::ROWB / 1024 + (Q16_ ? 2 : 0);
   static constexpr int STORES = PartialRec<D>::STORES;    // previous unit's record
   static_assert(16 % RING == 0, "slots repeat every split");
   static_assert(LOADS * (AHEAD - 1) + STORES + QLOADS <= 63, "vmcnt range");
@@ -691,6 +693,20 @@ struct StreamSrc {
   DecodeUnit<D> cur, nxt;
   bool has_next;
   bool first;  // the wave's first unit: no record stores precede its chunks
+  // int16 cache: LDS addresses of the current unit's 256 key / value factors
+  uint32_t kscl = 0, vscl = 0;
+  __device__ __forceinline__ void factors(uint32_t base, int C, float (&f)[8]) const {
+    const int q = (threadIdx.x & (kWave - 1)) >> 4;
+    const uint32_t a = base + (uint32_t)(32 * C + 8 * q) * 4;
+    const f32x4 x = *(lds_f32x4*)(uintptr_t)a, y = *(lds_f32x4*)(uintptr_t)(a + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[j] = x[j];
+      f[4 + j] = y[j];
+    }
+  }
+  __device__ __forceinline__ void kscale(int C, float (&f)[8]) const { factors(kscl, C, f); }
+  __device__ __forceinline__ void vscale(int C, float (&f)[8]) const { factors(vscl, C, f); }
 
   // stream position G: chunk G of the current unit (G < 16) or chunk G-16 of
   // the next one; K chunks are 0..7, V chunks 8..15
@@ -787,6 +803,34 @@ __device__ __forceinline__ void copy_q(const uint16_t* q, int b, int g, int nq, 
     lds_dma16_sv(base, (uint32_t)((src_col * D + logical * 8) * 2), slot + (uint32_t)n * 1024);
   }
 }
+// Lane I of x takes the wave-uniform value v (v_writelane_b32; the lane
+// select is an inline constant).
+template <int I>
+__device__ __forceinline__ void write_lane(int& x, int v) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(x) : "s"(v), "i"(I));
+}
+
+// The key and value factors of a decode unit's 256 keys (int16 cache) into
+// LDS: lane l brings keys key0 + 4l .. +3, slots 4(l%4).. of page pg[l/4]
+// (for a split past the last position the page is the last one's; those
+// keys' factors are never used).  Two direct loads of 1 KiB.
+template <int D>
+__device__ __forceinline__ void copy_factors(const float* kf, const float* vf,
+                                             const DecodeUnit<D>& un, int nkv, uint32_t slot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  // lane i of `held` holds pg[i] (the pages are wave-uniform); lane l then
+  // reads lane l/4's value.  (A select chain over pg here is turned into an
+  // indexed access, which would put the whole unit in scratch memory.)
+  int held = 0;
+  static_for<0, 16>([&](auto ic) __attribute__((always_inline)) {
+    write_lane<decltype(ic)::value>(held, un.sp.pg[decltype(ic)::value]);
+  });
+  const int page = __builtin_amdgcn_ds_bpermute((lane >> 2) << 2, held);
+  const uint32_t off = (uint32_t)((((int64_t)page * nkv + un.g) * 16 + 4 * (lane & 3)) * 4);
+  lds_dma16_sv(kf, off, slot);
+  lds_dma16_sv(vf, off, slot + 1024);
+}
+
 template <int D>
 __device__ __forceinline__ void read_q(const uint8_t* slot, bf16x8 (&qf)[KV<D>::DS]) {
   const int lane = threadIdx.x & (kWave - 1), col = lane & 15, q4 = lane >> 4;
@@ -795,15 +839,21 @@ __device__ __forceinline__ void read_q(const uint8_t* slot, bf16x8 (&qf)[KV<D>::
     qf[t] = as_bf16x8(*(const u32x4*)(slot + col * KV<D>::ROWB + (((4 * t + q4) ^ qswz<D>(col)) << 4)));
 }
 
-template <int D, int WAVES, int RING>
-__global__ __launch_bounds__(64 * WAVES) void bi_attn_decode_partial_kernel(
+// Q16: the cache holds int16 codes with per-(page, kv head, slot) factors kf /
+// vf; each unit's 256 key and value factors travel with its q copy into a
+// double-buffered 2 KiB LDS slot of the wave.
+template <int D, int WAVES, int RING, bool Q16>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bi_attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
-    int smax, float c2) {
-  using Src = StreamSrc<D, RING>;
+    int smax, float c2, const float* __restrict__ kf, const float* __restrict__ vf) {
+  using Src = StreamSrc<D, RING, Q16>;
   constexpr int QSLOT = 16 * KV<D>::ROWB;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[WAVES][Src::RING * Src::SLOT + 2 * QSLOT];
+  constexpr int FSLOT = Q16 ? 2048 : 0;  // key factors, then value factors
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[WAVES][Src::RING * Src::SLOT + 2 * QSLOT + 2 * FSLOT];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t NW = (int64_t)gridDim.x * WAVES;
@@ -811,6 +861,7 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_decode_partial_kernel(
   const int group = nq / nkv;
   const uint8_t* ring = lds[wave];
   const uint32_t qslot0 = (uint32_t)(uintptr_t)(ring + Src::RING * Src::SLOT);
+  const uint32_t fslot0 = qslot0 + 2 * QSLOT;
 
   // Units are dealt round-robin from the list of existing ones only, so every
   // wave gets the same number (+-1).  The list is sequence-major; sequence b
@@ -886,6 +937,7 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_decode_partial_kernel(
   fill(src.cur, u);
   int qi = 0;
   copy_q<D>(q, src.cur.b, src.cur.g, nq, group, qslot0);
+  if constexpr (Q16) copy_factors<D>(kf, vf, src.cur, nkv, fslot0);
   src.prologue();
   const int col = lane & 15;
   const bool live = col < group;
@@ -895,6 +947,8 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_decode_partial_kernel(
     if (src.has_next) {
       fill(src.nxt, un);
       copy_q<D>(q, src.nxt.b, src.nxt.g, nq, group, qslot0 + (uint32_t)(qi ^ 1) * QSLOT);
+      if constexpr (Q16)
+        copy_factors<D>(kf, vf, src.nxt, nkv, fslot0 + (uint32_t)(qi ^ 1) * FSLOT);
     }
     // Wait for this unit's q copy.  Issued after it: the unit's first AHEAD
     // chunks, the previous unit's record stores (unless this is the wave's
@@ -911,6 +965,10 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_decode_partial_kernel(
     }
     bf16x8 qf[1][KV<D>::DS];
     read_q<D>(ring + Src::RING * Src::SLOT + qi * QSLOT, qf[0]);
+    if constexpr (Q16) {
+      src.kscl = fslot0 + (uint32_t)qi * FSLOT;
+      src.vscl = src.kscl + 1024;
+    }
     const int L = src.cur.last + 1;
     const int pcol[1] = {L - 1};
     u32x4 p[1][8];
@@ -1364,25 +1422,33 @@ static int decode_workgroups(int64_t units) {
 
 hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
                               const int32_t* bt, const void* kc, const void* vc, void* out,
-                              float* lse, int max_splits, float* ws, hipStream_t st) {
+                              float* lse, int max_splits, float* ws, hipStream_t st,
+                              const float* kf, const float* vf) {
   const int64_t units = (int64_t)s.B * s.nkv * max_splits;
   const dim3 grid1((unsigned)decode_workgroups(units)), grid2((unsigned)((int64_t)s.B * s.nq));
   const float c2 = base2_scale(s.scale);
+  const bool q16 = kf != nullptr;
+#define BI_DECODE(DD, QQ)                                                                        \
+  hipLaunchKernelGGL((bi_attn_decode_partial_kernel<DD, kDecodeWaves, kDecodeSlots, QQ>), grid1, \
+                     dim3(64 * kDecodeWaves), 0, st, (const uint16_t*)q, kv_len, bt,             \
+                     (const uint16_t*)kc, (const uint16_t*)vc, ws, s.B, s.nq, s.nkv, s.max_pages, \
+                     max_splits, c2, kf, vf)
   if (s.d == 128) {
-    hipLaunchKernelGGL((bi_attn_decode_partial_kernel<128, kDecodeWaves, kDecodeSlots>), grid1,
-                       dim3(64 * kDecodeWaves), 0, st,
-                       (const uint16_t*)q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
-                       ws, s.B, s.nq, s.nkv, s.max_pages, max_splits, c2);
+    if (q16)
+      BI_DECODE(128, true);
+    else
+      BI_DECODE(128, false);
     hipLaunchKernelGGL(bi_attn_combine_kernel<128>, grid2, dim3(128), 0, st, (const float*)ws,
                        kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
   } else {
-    hipLaunchKernelGGL((bi_attn_decode_partial_kernel<64, kDecodeWaves, kDecodeSlots>), grid1,
-                       dim3(64 * kDecodeWaves), 0, st,
-                       (const uint16_t*)q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
-                       ws, s.B, s.nq, s.nkv, s.max_pages, max_splits, c2);
+    if (q16)
+      BI_DECODE(64, true);
+    else
+      BI_DECODE(64, false);
     hipLaunchKernelGGL(bi_attn_combine_kernel<64>, grid2, dim3(64), 0, st, (const float*)ws,
                        kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
   }
+#undef BI_DECODE
   return hipGetLastError();
 }
 

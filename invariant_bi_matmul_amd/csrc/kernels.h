@@ -61,7 +61,8 @@ hipError_t launch_kv_append_i16(const AttnDims& s, const void* k_new, const void
                                 hipStream_t st);
 hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
                               const int32_t* bt, const void* kc, const void* vc, void* out,
-                              float* lse, int max_splits, float* ws, hipStream_t st);
+                              float* lse, int max_splits, float* ws, hipStream_t st,
+                              const float* kf = nullptr, const float* vf = nullptr);
 hipError_t launch_attn_decode_splitkv(const AttnDims& s, const void* q, const int32_t* kv_len,
                                       const int32_t* bt, const void* kc, const void* vc, void* out,
                                       float* lse, int max_kv_len, int num_splits, float* ws,

@@ -43,11 +43,11 @@ def test_debug_build_exports_the_same_functions():
     dbg = ctypes.CDLL(_build.DEBUG_LIB)
     for n in declared_functions():
         assert hasattr(dbg, n), n
-    assert dbg.bi_abi_version() == 1
+    assert dbg.bi_abi_version() == 2
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bi_abi_version() == 1
+    assert lib.bi_abi_version() == 2
     for s in range(7):
         assert lib.bi_status_string(s)
     assert lib.bi_status_string(99) == b"unknown status"

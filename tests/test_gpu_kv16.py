@@ -82,8 +82,9 @@ def test_codes_and_parity(nq, nkv, d, L):
     assert rel_err(synth.bf16_to_f32(_bits(out)), ref) < TOL_BF16
 
 
-def test_chunked_prefill_and_decode_equal_one_shot():
-    nq, nkv, d, L, P = 32, 8, 128, 600, 540
+@pytest.mark.parametrize("nq,nkv,d", [(32, 8, 128), (8, 2, 64)])
+def test_chunked_prefill_and_decode_equal_one_shot(nq, nkv, d):
+    L, P = 600, 540
     scale = float(np.float32(1 / np.sqrt(d)))
     q, k, v = _seq(L, nq, nkv, d, 1, "kv16.c")
     one = _bits(_prefill(Cache(64, nkv, d, 1), [0], [L], [0], [q], [k], [v], scale))
@@ -101,16 +102,22 @@ def test_chunked_prefill_and_decode_equal_one_shot():
     assert np.array_equal(np.concatenate(got), one)
 
 
-def test_decode_alone_equals_decode_in_a_batch():
+@pytest.mark.parametrize("nb", [5, 300])
+def test_decode_alone_equals_decode_in_a_batch(nb):
+    """A sequence's decode row is the same alone and among nb - 1 others (300
+    sequences: past the decode kernel's balanced unit list)."""
     nq, nkv, d = 32, 8, 128
     scale = float(np.float32(1 / np.sqrt(d)))
     lens = [700, 33, 1200, 257, 500]
+    if nb > len(lens):
+        lens += synth.stream(9, "kv16.lens").integers(2, 120, size=nb - len(lens)).tolist()
     seqs = [_seq(L, nq, nkv, d, 3, "kv16.b%d" % i) for i, L in enumerate(lens)]
     # everything but the last token of every sequence, then one decode step
     alone = Cache(512, nkv, d, 3)
     _prefill(alone, [2], [lens[2] - 1], [0], [seqs[2][0]], [seqs[2][1]], [seqs[2][2]], scale)
-    batch = Cache(512, nkv, d, 4)
-    _prefill(batch, list(range(5)), [L - 1 for L in lens], [0] * 5, [s[0] for s in seqs],
+    batch = Cache(sum((L + 15) // 16 for L in lens) + 16, nkv, d, 4)
+    n = len(lens)
+    _prefill(batch, list(range(n)), [L - 1 for L in lens], [0] * n, [s[0] for s in seqs],
              [s[1] for s in seqs], [s[2] for s in seqs], scale)
 
     def step(cache, idx):
@@ -123,5 +130,5 @@ def test_decode_alone_equals_decode_in_a_batch():
             cache.vc, cache.kf, cache.vf, scale))
 
     a = step(alone, [2])
-    b = step(batch, list(range(5)))
+    b = step(batch, list(range(n)))
     assert np.array_equal(a[0], b[2])
