@@ -665,6 +665,10 @@ __global__ __launch_bounds__(64) void kv_append_i16_kernel(
 // call).
 // Workspace record per (b, q head, s): o[D], m, l, 2 pad floats (fp32).
 constexpr int kDecodeWaves = 2, kDecodeSlots = 8;  // slots divide the 16 chunks of a split
+// The int16 cache's unpacking makes its units VALU-bound rather than
+// HBM-bound: three waves per CU with a 4-slot ring each (the LDS holds no
+// more), so three SIMDs do that work.
+constexpr int kDecodeWaves16 = 3, kDecodeSlots16 = 4;
 constexpr int kMapSeqs = 256;  // batches up to this size get the balanced unit list
 
 template <int D>
@@ -1414,9 +1418,9 @@ hipError_t launch_kv_append_i16(const AttnDims& s, const void* k_new, const void
 
 // Workgroups of the persistent decode kernel: one per CU (each uses most of
 // a CU's LDS), fewer when there are fewer units.
-static int decode_workgroups(int64_t units) {
+static int decode_workgroups(int64_t units, int waves) {
   const int cus = device_cus();
-  const int64_t need = (units + kDecodeWaves - 1) / kDecodeWaves;
+  const int64_t need = (units + waves - 1) / waves;
   return (int)(need < cus ? need : cus);
 }
 
@@ -1425,12 +1429,15 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* k
                               float* lse, int max_splits, float* ws, hipStream_t st,
                               const float* kf, const float* vf) {
   const int64_t units = (int64_t)s.B * s.nkv * max_splits;
-  const dim3 grid1((unsigned)decode_workgroups(units)), grid2((unsigned)((int64_t)s.B * s.nq));
-  const float c2 = base2_scale(s.scale);
   const bool q16 = kf != nullptr;
+  const int waves = q16 ? kDecodeWaves16 : kDecodeWaves;
+  const dim3 grid1((unsigned)decode_workgroups(units, waves)),
+      grid2((unsigned)((int64_t)s.B * s.nq));
+  const float c2 = base2_scale(s.scale);
 #define BI_DECODE(DD, QQ)                                                                        \
-  hipLaunchKernelGGL((bi_attn_decode_partial_kernel<DD, kDecodeWaves, kDecodeSlots, QQ>), grid1, \
-                     dim3(64 * kDecodeWaves), 0, st, (const uint16_t*)q, kv_len, bt,             \
+  hipLaunchKernelGGL((bi_attn_decode_partial_kernel<DD, QQ ? kDecodeWaves16 : kDecodeWaves,      \
+                                                    QQ ? kDecodeSlots16 : kDecodeSlots, QQ>),    \
+                     grid1, dim3(64 * waves), 0, st, (const uint16_t*)q, kv_len, bt,             \
                      (const uint16_t*)kc, (const uint16_t*)vc, ws, s.B, s.nq, s.nkv, s.max_pages, \
                      max_splits, c2, kf, vf)
   if (s.d == 128) {
