@@ -852,32 +852,43 @@ def main():
     comp["attn_prefill"]["mfma_frac"] = comp["attn_prefill"]["TFLOP/s"] / MFMA_BF16_PEAK
     comp["attn_decode"]["hbm_frac"] = comp["attn_decode"]["GB/s"] / HBM_PEAK_GBS
     extras = {}
+
+    def extra(name, fn):
+        """Run one optional measurement; a failure is recorded in the line
+        instead of losing the step's numbers."""
+        try:
+            extras[name] = fn()
+        except Exception as e:  # noqa: BLE001 - reported, never hidden
+            log("bench: %s failed: %r" % (name, e))
+            extras[name] = {"error": repr(e)}
+
     if not args.no_extras:
         log("bench: invariance check and comparators")
-        extras["invariance_bitwise"] = invariance_check(wl)
-        extras["cost_of_invariance"] = comparators(wl)
+        extra("invariance_bitwise", lambda: invariance_check(wl))
+        extra("cost_of_invariance", lambda: comparators(wl))
         log("bench: other sizes")
-        extras["more_sizes"] = more_sizes(wl)
+        extra("more_sizes", lambda: more_sizes(wl))
         if not args.no_sweeps:
             log("bench: measured ceilings")
-            extras["ceilings"] = ceilings()
+            extra("ceilings", ceilings)
             c = extras["ceilings"]
-            extras["vs_measured_ceilings"] = {
-                "matmul_over_mfma_loop": tflops / c["mfma_bf16_loop"]["TFLOP/s"],
-                "decode_over_read_stream": comp["attn_decode"]["GB/s"] / c["read_4GiB"]["GB/s"],
-                "rmsnorm_over_copy": comp["rmsnorm"]["GB/s"] / c["copy_4GiB"]["GB/s"]}
+            if "error" not in c:
+                extras["vs_measured_ceilings"] = {
+                    "matmul_over_mfma_loop": tflops / c["mfma_bf16_loop"]["TFLOP/s"],
+                    "decode_over_read_stream": comp["attn_decode"]["GB/s"] / c["read_4GiB"]["GB/s"],
+                    "rmsnorm_over_copy": comp["rmsnorm"]["GB/s"] / c["copy_4GiB"]["GB/s"]}
             log("bench: size sweeps")
-            extras["sweeps"] = sweeps(wl)
+            extra("sweeps", lambda: sweeps(wl))
         if not args.no_e2e:
             log("bench: end-to-end Llama-8B-shaped stack, alone vs 63 companions")
-            extras["e2e_llama8b"] = e2e_llama8b()
+            extra("e2e_llama8b", e2e_llama8b)
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: oracle on the host")
         cpu = cpu_baseline(wl)
         if not args.no_extras:
             log("bench: oracle on all cores and on one")
-            extras["cpu_oracle"] = cpu_oracle(wl)
+            extra("cpu_oracle", lambda: cpu_oracle(wl))
     traffic = traffic_for("matmul.hip")
     line = {
         "metric": "invariant matmul TFLOP/s + RMSNorm/attn GB/s (% roofline), bitwise row-invariance",

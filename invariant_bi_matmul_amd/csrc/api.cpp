@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -55,10 +57,14 @@ int debug_check_tables(const bi_attn_shape* s, const int32_t* kv_len, const int3
                        const int32_t* bt, int max_len, int max_q, int64_t total_q,
                        hipStream_t st) {
   static int* flags[64] = {};  // one device int per device, allocated once
+  static std::mutex alloc;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BI_ERR_HIP;
-  if (flags[dev] == nullptr && hipMalloc((void**)&flags[dev], sizeof(int)) != hipSuccess)
-    return BI_ERR_HIP;
+  {
+    std::lock_guard<std::mutex> lock(alloc);
+    if (flags[dev] == nullptr && hipMalloc((void**)&flags[dev], sizeof(int)) != hipSuccess)
+      return BI_ERR_HIP;
+  }
   if (bi::launch_check_attn_tables(kv_len, cu_q, bt, s->num_seqs, s->max_pages_per_seq,
                                    s->num_pages, max_len, max_q, total_q, flags[dev], st) !=
       hipSuccess)
