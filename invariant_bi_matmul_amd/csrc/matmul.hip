@@ -3,12 +3,16 @@
 // bi_matmul_kernel follows the MatMul row of the approach table in "Defeating
 // Nondeterminism in LLM Inference" (mobiles-han.blogspot.com summary): one
 // kernel configuration, compiled ahead, is used for every shape and batch
-// size.  Here that is one tile (BM x BN x BK = 256 x 128 x 64, eight wave64s of
-// 64 x 64 each), one MFMA instruction (v_mfma_f32_32x32x16_bf16), one k order
-// (k-tiles ascending, 16-wide MFMA steps ascending inside a tile) and no
-// split-K.  M only decides how many tiles exist; rows past M are computed from
-// a clamped (valid) row and never stored, and MFMA rows do not interact, so a
-// row's bits are the same for every M and every position in a tile.
+// size.  Here the configuration is what decides an element's bits: one MFMA
+// instruction (v_mfma_f32_32x32x16_bf16), one k order (64-wide k-tiles
+// ascending, 16-wide MFMA steps ascending inside a tile) and no split-K.  The
+// main tile is BM x BN x BK = 256 x 128 x 64 (eight wave64s of 64 x 64 each);
+// launches too small to give it every CU use 128 x 128 or 64 x 64 tiles of the
+// same kernel.  A tile only decides which wave computes an element: its row
+// and column sit at their index mod 32 inside a 32 x 32 MFMA block under every
+// tile, and MFMA rows and columns do not interact.  Rows past M are computed
+// from a clamped (valid) row and never stored.  So a row's bits are the same
+// for every M, every tile and every position in a tile.
 //
 // Data path per k-tile: global -> LDS by direct loads (global_load_lds, 16
 // bytes per lane, no register staging) into a three-stage ring -> MFMA
@@ -44,6 +48,7 @@
 // bix_matmul_* is the non-invariant comparator from the problem column of the
 // same row: split-K with a split count chosen from the grid size (so from M),
 // fp32 partials summed by a second kernel.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -52,8 +57,10 @@
 namespace bi {
 namespace {
 
-struct Tile {
-  static constexpr int BM = 256, BN = 128, BK = kMatmulBK, WAVES_M = 4, WAVES_N = 2, STAGES = 3;
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = kMatmulBK, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_,
+                       STAGES = STAGES_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 32, NI = WN / 32;
   static constexpr int KS = BK / 16;                  // MFMA k-steps per k-tile
@@ -65,7 +72,7 @@ struct Tile {
   static constexpr int A_CPR = BK / 8, W_CPR = BN / 8;  // 16-byte chunks per row
   static constexpr int GROUP_M = 4;                   // row-tiles per raster group
   static_assert(BK == 64, "swizzles assume 128-byte A rows");
-  static_assert(BN >= 128, "W swizzle needs 16 chunks per k row");
+  static_assert(BN == 128 || BN == 64, "W swizzles exist for 16 and 8 chunks per k row");
   static_assert(A_LOADS * NT * 16 == A_BYTES && W_LOADS * NT * 16 == W_BYTES, "tile/threads");
   static_assert(MI * 32 == WM && NI * 32 == WN, "wave tile");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS");
@@ -76,26 +83,44 @@ struct Tile {
   static constexpr int a_bytes(int na) { return na * NT * 16; }
   static constexpr int stage_bytes(int na) { return a_bytes(na) + W_BYTES; }
   static constexpr int ring(int na) { return STAGES * STAGE / stage_bytes(na); }
+  // the single-row-tile variants (live row blocks, fewer A loads) need two
+  // 32-row blocks per wave and A load i filling rows 64i .. 64i+63
+  static constexpr bool LIVE_VARIANTS = MI == 2 && A_LOADS == 4 && BM / A_LOADS == 64;
 };
+// The main tile, and two smaller ones for launches whose main-tile grid would
+// leave CUs idle: 128 x 128 (four 64 x 64 waves, one per SIMD) and 64 x 64
+// (four 32 x 32 waves; two workgroups share a CU).
+using Tile = TileCfg<256, 128, 4, 2, 3>;
+using TileM = TileCfg<128, 128, 2, 2, 3>;
+using TileS = TileCfg<64, 64, 2, 2, 4>;
 
 // A in LDS: [BM rows][8 chunks of 16 B]; chunk c of row r sits at
 // c ^ swz_a(r): the 8 rows an MFMA operand read touches per 128-byte window
 // fall on 8 different 16-byte bank groups.
 __device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
-// W in LDS: [BK k rows][16 chunks of 16 B]; chunk c of k row k sits at
-// c ^ swz_w(k) (64-byte block XOR).
-__device__ __forceinline__ int swz_w(int k) { return (k & 3) << 2; }
+// W in LDS: [BK k rows][CPR chunks of 16 B]; chunk c of k row k sits at
+// c ^ swz_w(k), a 64-byte block XOR.  A half-wave's transposing read covers 4
+// consecutive k rows (from a multiple of 4) and 64 bytes of each; the XOR
+// puts those four 64-byte pieces on four different quarters of the 256-byte
+// bank space: by k mod 4 for 256-byte rows (CPR 16), and by bit 1 of k for
+// 128-byte rows (CPR 8), whose row pairs already differ by 128 bytes.
+template <int CPR>
+__device__ __forceinline__ int swz_w(int k) {
+  if constexpr (CPR == 16) return (k & 3) << 2;
+  else return ((k >> 1) & 1) << 2;
+}
 
 // Position of raster id `id` (groups of GROUP_M row-tiles; row-tiles fastest
 // inside a group, then columns).
+template <class T>
 __device__ __forceinline__ void raster_tile(uint32_t id, int tiles_m, int tiles_n, int& m0,
                                             int& n0) {
-  const uint32_t per_group = (uint32_t)Tile::GROUP_M * (uint32_t)tiles_n;
+  const uint32_t per_group = (uint32_t)T::GROUP_M * (uint32_t)tiles_n;
   const int grp = (int)(id / per_group);
-  const int grp_rows = min(Tile::GROUP_M, tiles_m - grp * Tile::GROUP_M);
+  const int grp_rows = min(T::GROUP_M, tiles_m - grp * T::GROUP_M);
   const uint32_t within = id - (uint32_t)grp * per_group;
-  m0 = (grp * Tile::GROUP_M + (int)(within % (uint32_t)grp_rows)) * Tile::BM;
-  n0 = (int)(within / (uint32_t)grp_rows) * Tile::BN;
+  m0 = (grp * T::GROUP_M + (int)(within % (uint32_t)grp_rows)) * T::BM;
+  n0 = (int)(within / (uint32_t)grp_rows) * T::BN;
 }
 
 // Persistent: the invariant launch has about one workgroup per CU.  Workgroup
@@ -106,12 +131,11 @@ __device__ __forceinline__ void raster_tile(uint32_t id, int tiles_m, int tiles_
 // tiles back to back through one continuous stream of k-tiles: the ring
 // loads the next tile's first k-tiles while the current tile finishes.  The
 // split-K comparator launches one workgroup per (tile, slice) instead.
-template <bool SPLIT>
-__global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __restrict__ A,
+template <class T, bool SPLIT>
+__global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ W,
                                                              void* __restrict__ C, int M, int N,
                                                              int K, int out_f32, int kt_per_split) {
-  using T = Tile;
   constexpr int BK = T::BK, NT = T::NT, KS = T::KS, STAGES = T::STAGES;
   constexpr int MI = T::MI, NI = T::NI, STAGE = T::STAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
@@ -215,7 +239,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   if (nk <= 0) {  // K = 0: every tile is zero
     for (uint32_t t = 0; t < count; ++t) {
       int m0, n0;
-      raster_tile(first + t * step, tiles_m, tiles_n, m0, n0);
+      raster_tile<T>(first + t * step, tiles_m, tiles_n, m0, n0);
       store_tile(m0, n0, acc);
     }
     return;
@@ -231,7 +255,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   const uint8_t* w_base;
   auto load_tile = [&](uint32_t t) __attribute__((always_inline)) {
     int m0, n0;
-    raster_tile(first + t * step, tiles_m, tiles_n, m0, n0);
+    raster_tile<T>(first + t * step, tiles_m, tiles_n, m0, n0);
 #pragma unroll
     for (int i = 0; i < T::A_LOADS; ++i) {
       const int q = i * NT + wave * 64 + lane;
@@ -241,7 +265,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
 #pragma unroll
     for (int i = 0; i < T::W_LOADS; ++i) {
       const int q = i * NT + wave * 64 + lane;
-      const int k = q / T::W_CPR, c = (q % T::W_CPR) ^ swz_w(q / T::W_CPR);
+      const int k = q / T::W_CPR, c = (q % T::W_CPR) ^ swz_w<T::W_CPR>(q / T::W_CPR);
       w_off[i] = (uint32_t)(((int64_t)k * N + min(n0 + c * 8, N - 8) - n0) * 2);
     }
     a_base = (const uint8_t*)(A + (int64_t)m0 * K);
@@ -303,7 +327,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   for (int ni = 0; ni < NI; ++ni) {
     const int nb = wave_n * T::WN + ni * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
     const int k = 8 * (g16 >> 1) + (i16 >> 2);
-    wo[ni] = (uint32_t)(k * T::W_ROW + (((nb >> 3) ^ swz_w(k)) << 4) + (nb & 7) * 2);
+    wo[ni] = (uint32_t)(k * T::W_ROW + (((nb >> 3) ^ swz_w<T::W_CPR>(k)) << 4) + (nb & 7) * 2);
   }
 
   // fragments of k-step kk from the stage at S: the first NB row blocks of A
@@ -329,7 +353,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   uint32_t ct = 0;  // tile being accumulated
   int ckt = 0;      // its k-tiles done
   int cm0, cn0;
-  raster_tile(first, tiles_m, tiles_n, cm0, cn0);
+  raster_tile<T>(first, tiles_m, tiles_n, cm0, cn0);
   // One k-tile j held in stage S.  Its step-0 fragments were read during the
   // previous k-tile's last step.  Steps 0..KS-2 read the next step's
   // fragments under their MFMAs and issue load groups 1.. of k-tile j+2 (into
@@ -353,10 +377,8 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   // In the same case the A loads that would fill only rows past M are not
   // issued either: NA = 1 (M <= 64), 2 (M <= 128) or all 4 A loads per k-tile.
   // Every row an MFMA of a live block reads lies below 64 * ceil(M / 64).
-  static_assert(MI == 2, "the live-block variants assume two 32-row blocks per wave");
-  static_assert(T::A_LOADS == 4 && T::BM / T::A_LOADS == 64, "A load i fills rows 64i..64i+63");
   int live = MI, na = T::A_LOADS;
-  if (tiles_m == 1) {
+  if (T::LIVE_VARIANTS && tiles_m == 1) {
     const int rows = M - wave_m * T::WM;
     live = __builtin_amdgcn_readfirstlane(rows <= 0 ? 0 : (rows >= MI * 32 ? MI : (rows + 31) / 32));
     na = M <= 64 ? 1 : (M <= 128 ? 2 : T::A_LOADS);
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
       ckt = 0;
-      if (++ct < count) raster_tile(first + ct * step, tiles_m, tiles_n, cm0, cn0);
+      if (++ct < count) raster_tile<T>(first + ct * step, tiles_m, tiles_n, cm0, cn0);
     }
   };
   if (count == 0) return;
@@ -447,14 +469,16 @@ __global__ __launch_bounds__(Tile::NT) void bi_matmul_kernel(const uint16_t* __r
   };
   // one variant for the whole launch: (live blocks of this wave, A loads)
   auto run_live = [&](auto nc) __attribute__((always_inline)) {
-    if (live == MI)
+    if (!T::LIVE_VARIANTS || live == MI)
       run(std::integral_constant<int, MI>{}, nc);
-    else if (live == 1)
-      run(std::integral_constant<int, 1>{}, nc);
-    else
-      run(std::integral_constant<int, 0>{}, nc);
+    else if constexpr (T::LIVE_VARIANTS) {
+      if (live == 1)
+        run(std::integral_constant<int, 1>{}, nc);
+      else
+        run(std::integral_constant<int, 0>{}, nc);
+    }
   };
-  if constexpr (SPLIT) {  // the comparator keeps the one full ring
+  if constexpr (SPLIT || !T::LIVE_VARIANTS) {  // the comparator keeps the one full ring
     run_live(std::integral_constant<int, T::A_LOADS>{});
   } else {
     if (na == 1)
@@ -498,13 +522,38 @@ static int device_cus() {
   return cus;
 }
 
-hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
-                         int64_t k, hipStream_t st) {
-  const int64_t tiles = ((m + Tile::BM - 1) / Tile::BM) * ((n + Tile::BN - 1) / Tile::BN);
-  const int64_t grid = tiles < device_cus() ? tiles : device_cus();
-  hipLaunchKernelGGL((bi_matmul_kernel<false>), dim3((unsigned)grid), dim3(Tile::NT), 0, st,
+template <class T>
+static int64_t tile_count(int64_t m, int64_t n) {
+  return ((m + T::BM - 1) / T::BM) * ((n + T::BN - 1) / T::BN);
+}
+
+// The tile: 64 x 64 if its tiles number at most one per CU, else 128 x 128
+// under the same condition, else the main tile (persistent, at most one
+// workgroup per CU).  A smaller
+// tile moves more bytes per flop from L2 to LDS, and the 128 x 128 tile runs
+// one wave per SIMD; so past one round of tiles the main tile's fewer, denser
+// tiles finish first.  All three run the same MFMA instruction on the same
+// operands in the same k order for every output element (a row or column's
+// place inside a 32 x 32 block is its index mod 32 under each tile), so the
+// choice changes no bits.
+template <class T>
+static void launch_tile(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
+                        int64_t k, int64_t grid, hipStream_t st) {
+  hipLaunchKernelGGL((bi_matmul_kernel<T, false>), dim3((unsigned)grid), dim3(T::NT), 0, st,
                      (const uint16_t*)a, (const uint16_t*)w, c, (int)m, (int)n, (int)k,
                      c_f32 ? 1 : 0, 0);
+}
+
+hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
+                         int64_t k, hipStream_t st) {
+  const int64_t cus = device_cus();
+  const int64_t ts = tile_count<TileS>(m, n), tm = tile_count<TileM>(m, n);
+  if (ts <= cus)
+    launch_tile<TileS>(a, w, c, c_f32, m, n, k, ts, st);
+  else if (tm <= cus)
+    launch_tile<TileM>(a, w, c, c_f32, m, n, k, tm, st);
+  else
+    launch_tile<Tile>(a, w, c, c_f32, m, n, k, std::min(tile_count<Tile>(m, n), cus), st);
   return hipGetLastError();
 }
 
@@ -525,7 +574,7 @@ hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f3
   const int kt = (int)(k / Tile::BK);
   const int per = (kt + split_k - 1) / split_k;
   const int used = (kt + per - 1) / per;  // slices that own at least one k-tile
-  hipLaunchKernelGGL((bi_matmul_kernel<true>), dim3((unsigned)tiles, 1, (unsigned)used),
+  hipLaunchKernelGGL((bi_matmul_kernel<Tile, true>), dim3((unsigned)tiles, 1, (unsigned)used),
                      dim3(Tile::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
                      (int)m, (int)n, (int)k, 1, per);
   const int64_t count = m * n;
