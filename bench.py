@@ -458,7 +458,7 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
 
     matmul: M in {1,2,7,16,64,256,512,2048}, N in {4096, 14336}, K=4096:
     TFLOP/s, fraction of the bf16 peak, of the roofline min(peak, AI x 8 TB/s)
-    and the grid-fill ceiling of the fixed 256x128 tile; beside it the vendor
+    and the grid-fill ceiling of the tile bi_matmul picks; beside it the vendor
     GEMM (torch.matmul, not batch-invariant) on the same buffers.  RMSNorm: R in
     {1..16384 powers of two, 3, 7, 1000, 16383}, H in {4096, 8192}.  Decode:
     L in {512, 4096, 32768} x B in {1..64}, lengths ragged U{L/2..L} with one
@@ -489,11 +489,13 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
             by = 2.0 * (m * K + K * n + m * n)
             tf = flops / ms / 1e9
             roof = min(MFMA_BF16_PEAK, flops / by * HBM_PEAK_GBS / 1e3)
-            tiles = -(-m // 256) * (n // 128)
+            tm, tn, wgs = bi.matmul_tile(m, n)
+            tiles = -(-m // tm) * -(-n // tn)
             out["matmul"]["M%d_N%d" % (m, n)] = {
                 "ms": ms, "TFLOP/s": tf, "mfma_frac": tf / MFMA_BF16_PEAK,
                 "roofline_TFLOP/s": roof, "roofline_frac": tf / roof,
-                "GB/s": by / ms / 1e6, "tiles": tiles, "grid_fill_ceiling": _grid_fill(tiles),
+                "GB/s": by / ms / 1e6, "tile": "%dx%d" % (tm, tn), "tiles": tiles,
+                "workgroups": wgs, "grid_fill_ceiling": _grid_fill(tiles),
                 "vendor_ms": vms, "invariant_over_vendor": ms / vms, "graph_ms": gms}
             del cs
         del ws

@@ -103,14 +103,22 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t r
  * a  bf16 [m, k] row-major.
  * w  bf16 [k, n] row-major (n contiguous).
  * c  [m, n] row-major, bf16 (rounded from the fp32 sum) or fp32 per c_dtype.
- * One compiled tile and one bf16 MFMA instruction for every m, n, k; each
- * element's k-loop runs in one fixed order; no split-K.  The bf16 result is
- * exactly the round-to-nearest-even of the fp32 result.
+ * One bf16 MFMA instruction for every m, n, k; each element's k-loop runs in
+ * one fixed order (64-wide k-tiles, 16-wide MFMA steps, ascending); no
+ * split-K.  The output tile (256 x 128, or 128 x 128 / 64 x 64 for launches
+ * too small to give the main tile every CU; bix_matmul_tile reports it) only
+ * decides which wave computes an element, never its bits.  The bf16 result
+ * is exactly the round-to-nearest-even of the fp32 result.
  * Requires k % 64 == 0, n % 8 == 0, k <= 2^22 and n <= 2^24 (else
  * BI_ERR_UNSUPPORTED).
  */
 int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
               void* stream);
+
+/* The output tile bi_matmul uses for an m x n product on the current device
+ * (tile_m x tile_n) and the workgroups it launches.  Host-only; any pointer
+ * may be NULL.  BI_ERR_INVALID_SHAPE for m or n < 1. */
+int bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups);
 
 /* ------------------------------------------------------------------------- */
 /* Paged attention (approach table, Attention row: one unified cache layout,
@@ -336,7 +344,7 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
  * in fp32, in this order, as ONE bi_matmul over K' = 3K of the packed operands
  *     A3 = [hi(A) | hi(A) | lo(A)]  (bf16 [m, 3k], row by row)
  *     W3 = [hi(W) ; lo(W) ; hi(W)]  (bf16 [3k, n], stacked along k).
- * It inherits bi_matmul's invariance (one tile, one k order, no split-K) at
+ * It inherits bi_matmul's invariance (one MFMA, one k order, no split-K) at
  * three times its MFMA work; the error is about 2^-16 of sum |a||w| instead
  * of bf16's 2^-8. */
 

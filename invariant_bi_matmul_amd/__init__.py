@@ -20,7 +20,7 @@ __all__ = [
     "BIError", "lib_path", "debug_lib_path", "load", "load_library", "abi_version", "rmsnorm",
     "matmul", "attn_workspace_bytes",
     "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
-    "bix_rmsnorm_splitrow", "bix_matmul_splitk", "bix_attn_decode_splitkv",
+    "bix_rmsnorm_splitrow", "matmul_tile", "bix_matmul_splitk", "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
     "qkv_rope", "swiglu_pair",
     "attn_prefill_i16", "attn_decode_i16", "bix_mfma_loop",
@@ -91,6 +91,7 @@ def load_library(path: str):
         "bi_attn_prefill": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
         "bi_attn_decode": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, i32, P, sz, P]),
         "bix_rmsnorm_splitrow": (ctypes.c_int, [P, P, P, P, i64, i64, f32, i32, P, sz, P]),
+        "bix_matmul_tile": (ctypes.c_int, [i64, i64, P, P, P]),
         "bix_matmul_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "bix_matmul_splitk": (ctypes.c_int, [P, P, P, ctypes.c_int, i64, i64, i64, i32, P, sz, P]),
         "bix_attn_decode_workspace_bytes": (sz, [SP, i32, i32]),
@@ -215,6 +216,15 @@ def matmul(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
     code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
     _check("bi_matmul", load().bi_matmul(_ptr(a), _ptr(w), _ptr(c), code, m, n, k, _stream()))
     return c
+
+
+def matmul_tile(m: int, n: int):
+    """(tile_m, tile_n, workgroups) of bi_matmul for an m x n product on the
+    current device (bix_matmul_tile; host-only, launches nothing)."""
+    tm, tn, wg = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check("bix_matmul_tile", load().bix_matmul_tile(int(m), int(n), ctypes.byref(tm),
+                                                     ctypes.byref(tn), ctypes.byref(wg)))
+    return tm.value, tn.value, wg.value
 
 
 def bix_matmul_splitk(a, w, split_k: int = 0, out=None, out_dtype=torch.bfloat16,

@@ -187,6 +187,17 @@ int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int
   }
 }
 
+int bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups) {
+  if (m < 1 || n < 1) return BI_ERR_INVALID_SHAPE;
+  int bm, bn;
+  int64_t grid;
+  bi::matmul_tile(m, n, &bm, &bn, &grid);
+  if (tile_m != nullptr) *tile_m = bm;
+  if (tile_n != nullptr) *tile_n = bn;
+  if (workgroups != nullptr) *workgroups = grid;
+  return BI_OK;
+}
+
 size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k) {
   if (m < 0 || n < 0 || k < 0 || k % bi::kMatmulBK != 0) return 0;
   if (split_k <= 0) split_k = bi::matmul_splitk_auto(m, n, k);

@@ -18,6 +18,8 @@ int rmsnorm_splitrow_auto_chunks(int64_t rows);
 
 // ---- matmul ----------------------------------------------------------------
 constexpr int kMatmulBK = 64;
+// The tile launch_matmul uses for an m x n product (bm x bn) and its grid.
+void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid);
 hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
                          int64_t k, hipStream_t st);
 int matmul_splitk_auto(int64_t m, int64_t n, int64_t k);

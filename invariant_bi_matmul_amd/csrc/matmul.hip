@@ -544,16 +544,29 @@ static void launch_tile(const void* a, const void* w, void* c, bool c_f32, int64
                      c_f32 ? 1 : 0, 0);
 }
 
-hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
-                         int64_t k, hipStream_t st) {
+void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid) {
   const int64_t cus = device_cus();
   const int64_t ts = tile_count<TileS>(m, n), tm = tile_count<TileM>(m, n);
-  if (ts <= cus)
-    launch_tile<TileS>(a, w, c, c_f32, m, n, k, ts, st);
-  else if (tm <= cus)
-    launch_tile<TileM>(a, w, c, c_f32, m, n, k, tm, st);
+  if (ts <= cus) {
+    *bm = TileS::BM, *bn = TileS::BN, *grid = ts;
+  } else if (tm <= cus) {
+    *bm = TileM::BM, *bn = TileM::BN, *grid = tm;
+  } else {
+    *bm = Tile::BM, *bn = Tile::BN, *grid = std::min(tile_count<Tile>(m, n), cus);
+  }
+}
+
+hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
+                         int64_t k, hipStream_t st) {
+  int bm, bn;
+  int64_t grid;
+  matmul_tile(m, n, &bm, &bn, &grid);
+  if (bm == TileS::BM)
+    launch_tile<TileS>(a, w, c, c_f32, m, n, k, grid, st);
+  else if (bm == TileM::BM)
+    launch_tile<TileM>(a, w, c, c_f32, m, n, k, grid, st);
   else
-    launch_tile<Tile>(a, w, c, c_f32, m, n, k, std::min(tile_count<Tile>(m, n), cus), st);
+    launch_tile<Tile>(a, w, c, c_f32, m, n, k, grid, st);
   return hipGetLastError();
 }
 

@@ -82,6 +82,21 @@ def test_matmul_validation(lib):
     assert lib.bix_matmul_splitk(_p(), _p(), _p(), 0, 8, 4096, 4096, 4, _p(), 1024, None) == WS
 
 
+def test_matmul_tile_choice(lib):
+    """The tile bi_matmul picks (256 CUs, the MI355X count and the host-only
+    fallback): 64 x 64 while its tiles fit one per CU, then 128 x 128 under
+    the same rule, then the persistent 256 x 128 tile."""
+    import invariant_bi_matmul_amd as bi
+    cases = {(1, 4096): (64, 64, 64), (256, 4096): (64, 64, 256), (257, 4096): (128, 128, 96),
+             (1024, 4096): (128, 128, 256), (1025, 4096): (256, 128, 160),
+             (2048, 14336): (256, 128, 256), (64, 28672): (128, 128, 224),
+             (1, 128256): (256, 128, 256), (5, 8): (64, 64, 1)}
+    for (m, n), want in cases.items():
+        assert bi.matmul_tile(m, n) == want, (m, n)
+    assert lib.bix_matmul_tile(0, 4096, None, None, None) == SHAPE
+    assert lib.bix_matmul_tile(8, 4096, None, None, None) == OK
+
+
 def _shape(**kw):
     import invariant_bi_matmul_amd as bi
     base = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=128, max_pages_per_seq=4,
