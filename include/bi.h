@@ -105,7 +105,7 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t r
  * c  [m, n] row-major, bf16 (rounded from the fp32 sum) or fp32 per c_dtype.
  * One bf16 MFMA instruction for every m, n, k; each element's k-loop runs in
  * one fixed order (64-wide k-tiles, 16-wide MFMA steps, ascending); no
- * split-K.  The output tile (256 x 128, or 128 x 128 / 64 x 64 for launches
+ * split-K.  The output tile (256 x 128; 128 x 128, 128 x 64 or 64 x 64 for launches
  * too small to give the main tile every CU; bix_matmul_tile reports it) only
  * decides which wave computes an element, never its bits.  The bf16 result
  * is exactly the round-to-nearest-even of the fp32 result.

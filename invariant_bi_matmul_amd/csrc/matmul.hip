@@ -7,8 +7,8 @@
 // instruction (v_mfma_f32_32x32x16_bf16), one k order (64-wide k-tiles
 // ascending, 16-wide MFMA steps ascending inside a tile) and no split-K.  The
 // main tile is BM x BN x BK = 256 x 128 x 64 (eight wave64s of 64 x 64 each);
-// launches too small to give it every CU use 128 x 128 or 64 x 64 tiles of the
-// same kernel.  A tile only decides which wave computes an element: its row
+// launches too small to give it every CU use 128 x 128, 128 x 64 or 64 x 64
+// tiles of the same kernel.  A tile only decides which wave computes an element: its row
 // and column sit at their index mod 32 inside a 32 x 32 MFMA block under every
 // tile, and MFMA rows and columns do not interact.  Rows past M are computed
 // from a clamped (valid) row and never stored.  So a row's bits are the same
@@ -87,11 +87,12 @@ struct TileCfg {
   // 32-row blocks per wave and A load i filling rows 64i .. 64i+63
   static constexpr bool LIVE_VARIANTS = MI == 2 && A_LOADS == 4 && BM / A_LOADS == 64;
 };
-// The main tile, and two smaller ones for launches whose main-tile grid would
-// leave CUs idle: 128 x 128 (four 64 x 64 waves, one per SIMD) and 64 x 64
-// (four 32 x 32 waves; two workgroups share a CU).
+// The main tile, and three smaller ones for launches whose main-tile grid
+// would leave CUs idle: 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64
+// (four 64 x 32 waves) and 64 x 64 (four 32 x 32 waves).
 using Tile = TileCfg<256, 128, 4, 2, 3>;
 using TileM = TileCfg<128, 128, 2, 2, 3>;
+using TileN = TileCfg<128, 64, 2, 2, 4>;
 using TileS = TileCfg<64, 64, 2, 2, 4>;
 
 // A in LDS: [BM rows][8 chunks of 16 B]; chunk c of row r sits at
@@ -527,12 +528,12 @@ static int64_t tile_count(int64_t m, int64_t n) {
   return ((m + T::BM - 1) / T::BM) * ((n + T::BN - 1) / T::BN);
 }
 
-// The tile: 64 x 64 if its tiles number at most one per CU, else 128 x 128
-// under the same condition, else the main tile (persistent, at most one
-// workgroup per CU).  A smaller
-// tile moves more bytes per flop from L2 to LDS, and the 128 x 128 tile runs
-// one wave per SIMD; so past one round of tiles the main tile's fewer, denser
-// tiles finish first.  All three run the same MFMA instruction on the same
+// The tile: the first of 64 x 64, 128 x 64 and 128 x 128 whose tiles number at
+// most one per CU, else the main tile (persistent, at most one workgroup per
+// CU).  A smaller
+// tile moves more bytes per flop from L2 to LDS, and the smaller tiles run one
+// wave per SIMD; so past one round of tiles the main tile's fewer, denser
+// tiles finish first.  All four run the same MFMA instruction on the same
 // operands in the same k order for every output element (a row or column's
 // place inside a 32 x 32 block is its index mod 32 under each tile), so the
 // choice changes no bits.
@@ -546,9 +547,12 @@ static void launch_tile(const void* a, const void* w, void* c, bool c_f32, int64
 
 void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid) {
   const int64_t cus = device_cus();
-  const int64_t ts = tile_count<TileS>(m, n), tm = tile_count<TileM>(m, n);
+  const int64_t ts = tile_count<TileS>(m, n), tn = tile_count<TileN>(m, n);
+  const int64_t tm = tile_count<TileM>(m, n);
   if (ts <= cus) {
     *bm = TileS::BM, *bn = TileS::BN, *grid = ts;
+  } else if (tn <= cus) {
+    *bm = TileN::BM, *bn = TileN::BN, *grid = tn;
   } else if (tm <= cus) {
     *bm = TileM::BM, *bn = TileM::BN, *grid = tm;
   } else {
@@ -563,6 +567,8 @@ hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int6
   matmul_tile(m, n, &bm, &bn, &grid);
   if (bm == TileS::BM)
     launch_tile<TileS>(a, w, c, c_f32, m, n, k, grid, st);
+  else if (bm == TileN::BM && bn == TileN::BN)
+    launch_tile<TileN>(a, w, c, c_f32, m, n, k, grid, st);
   else if (bm == TileM::BM)
     launch_tile<TileM>(a, w, c, c_f32, m, n, k, grid, st);
   else

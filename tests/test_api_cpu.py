@@ -84,10 +84,11 @@ def test_matmul_validation(lib):
 
 def test_matmul_tile_choice(lib):
     """The tile bi_matmul picks (256 CUs, the MI355X count and the host-only
-    fallback): 64 x 64 while its tiles fit one per CU, then 128 x 128 under
-    the same rule, then the persistent 256 x 128 tile."""
+    fallback): the first of 64 x 64, 128 x 64, 128 x 128 whose tiles fit one
+    per CU, else the persistent 256 x 128 tile."""
     import invariant_bi_matmul_amd as bi
-    cases = {(1, 4096): (64, 64, 64), (256, 4096): (64, 64, 256), (257, 4096): (128, 128, 96),
+    cases = {(1, 4096): (64, 64, 64), (256, 4096): (64, 64, 256), (257, 4096): (128, 64, 192),
+             (512, 4096): (128, 64, 256), (513, 4096): (128, 128, 160),
              (1024, 4096): (128, 128, 256), (1025, 4096): (256, 128, 160),
              (2048, 14336): (256, 128, 256), (64, 28672): (128, 128, 224),
              (1, 128256): (256, 128, 256), (5, 8): (64, 64, 1)}

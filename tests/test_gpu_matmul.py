@@ -49,9 +49,11 @@ def test_row_invariance_across_m(n):
     wd = to_dev(w)
     full = _mm(a, None, w_dev=wd)
     # the workload's M, M on both sides of the single-row-tile variants (A
-    # loads for rows 0..63, 0..127, all 256), and M that select the 64 x 64,
-    # 128 x 128 and main tiles (N = 4096: up to 256, 257..1024, above)
-    for m in list(M_SET[:-1]) + [33, 65, 100, 128, 129, 200, 255, 257, 768, 1024, 1025, 1536]:
+    # loads for rows 0..63, 0..127, all 256), and M that select each tile
+    # (N = 4096: 64 x 64 up to 256, 128 x 64 to 512, 128 x 128 to 1024, then
+    # the main tile)
+    for m in list(M_SET[:-1]) + [33, 65, 100, 128, 129, 200, 255, 257, 513, 768, 1024, 1025,
+                                 1536]:
         c = _mm(a[:m], None, w_dev=wd)
         assert np.array_equal(c, full[:m]), m
     # a row at many different positions inside tiles and batches
