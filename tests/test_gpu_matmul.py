@@ -95,8 +95,14 @@ def test_one_hot_rows_select_w():
 
 
 @pytest.mark.parametrize("m,n,k", [(5, 8, 64), (33, 264, 128), (257, 520, 192), (1, 4104, 256),
-                                   (100, 264, 320), (64, 136, 64)])
+                                   (100, 264, 320), (64, 136, 64),
+                                   # ragged in both M and N under each larger tile
+                                   (500, 2056, 192), (1000, 2056, 128), (2100, 4104, 128)])
 def test_ragged_shapes(orc, m, n, k):
+    import invariant_bi_matmul_amd as bi
+    tile = {(500, 2056): (128, 64), (1000, 2056): (128, 128), (2100, 4104): (256, 128)}
+    if (m, n) in tile:
+        assert bi.matmul_tile(m, n)[:2] == tile[(m, n)]
     a, w = synth.matmul_inputs(m, n, k, seed=5)
     c = _mm(a, w)
     assert rel_err(f64(c), orc.matmul(a, w)) < TOL_BF16
