@@ -1022,14 +1022,15 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
       pl[j] = rs[D + 1];
       po[j] = rs[d];
     }
+    // the steps past the last split keep the state by a select, not a
+    // branch, so that the batch is one block the scheduler can interleave
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
-      if (s0 + j < ns) {
-        const FoldCoef f = fold_coef(m, pm[j]);
-        l = fold_apply(l, pl[j], f);
-        o = fold_apply(o, po[j], f);
-        m = f.m;
-      }
+      const bool ok = s0 + j < ns;
+      const FoldCoef f = fold_coef(m, pm[j]);
+      l = ok ? fold_apply(l, pl[j], f) : l;
+      o = ok ? fold_apply(o, po[j], f) : o;
+      m = ok ? f.m : m;
     }
   }
   out[bh * D + d] = (uint16_t)f32_to_bf16(o / l);
