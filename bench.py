@@ -788,6 +788,81 @@ def e2e_llama8b(steps: int = 128):
     return out
 
 
+METRIC = "invariant matmul TFLOP/s + RMSNorm/attn GB/s (% roofline), bitwise row-invariance"
+WORKLOAD = ("batch-invariant hot path step: RMSNorm [2048,4096] -> matmul [2048,4096]x[4096,14336]"
+            " -> attention prefill chunk 512 @ 4096 + decode B=64 ragged L<=4096, GQA 32/8, "
+            "d=128, 16-token pages")
+
+
+def _round(v, sig=4):
+    """Floats to `sig` significant digits, recursively (keeps the line short)."""
+    if isinstance(v, float):
+        return float("%.*g" % (sig, v)) if v == v else None
+    if isinstance(v, dict):
+        return {k: _round(x, sig) for k, x in v.items()}
+    if isinstance(v, (list, tuple)):
+        return [_round(x, sig) for x in v]
+    return v
+
+
+def _summary(extras):
+    """The extras that fit on the headline line: the invariance verdicts, each
+    comparator's time ratio and the end-to-end stack's verdicts and rates."""
+    out = {}
+    inv = extras.get("invariance_bitwise")
+    if isinstance(inv, dict):
+        out["invariance_bitwise"] = inv
+    coi = extras.get("cost_of_invariance")
+    if isinstance(coi, dict) and "error" not in coi:
+        out["cost_of_invariance"] = {
+            k: {r: x for r, x in v.items() if r.startswith("invariant_over")}
+            for k, v in coi.items() if isinstance(v, dict)}
+    e2e = extras.get("e2e_llama8b")
+    if isinstance(e2e, dict) and "error" not in e2e:
+        keep = ("tokens_equal", "logits_bitwise_equal", "batched64_tokens_per_s", "alone_s")
+        out["e2e_llama8b"] = {
+            name: {k: v for k, v in r.items() if k in keep or k.startswith("unique_outputs")}
+            for name, r in e2e.items() if name != "config" and isinstance(r, dict)}
+    for name, r in extras.items():
+        if isinstance(r, dict) and "error" in r:
+            out.setdefault("failed_extras", []).append(name)
+    return out
+
+
+def headline(steps, warmup, ms_step, tflops, comp, cpu, traffic, extras, extras_path):
+    """The one JSON line bench.py prints: the step's headline, its roofline
+    and host baseline, the four stages and a summary of the extras (a few KB
+    at most; the full record goes to `extras_path`)."""
+    keep = ("ms", "graph_ms", "GB/s", "TFLOP/s", "hbm_frac", "mfma_frac")
+    line = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Llama-8B-shaped tensors, random-init weights)",
+        "config": {"workload": WORKLOAD, "M": M, "K": K, "N": N, "decode_batch": B_DEC,
+                   "max_kv_len": L_MAX, "prefill_chunk": PREFILL_CHUNK},
+        "roofline": {"bound": "mfma", "kernel": "bi_matmul_kernel", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "components": {k: {f: v for f, v in c.items() if f in keep} for k, c in comp.items()},
+    }
+    line = _round(line)
+    line["value"] = tflops
+    line["ms_per_step"] = ms_step
+    line.update(_round(_summary(extras)))
+    line["extras_file"] = extras_path
+    return line
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -805,6 +880,9 @@ def main():
     ap.add_argument("--sweep-parts", default="matmul,rmsnorm,decode,prefill",
                     help="with --only sweeps: which sweeps, comma-separated")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--extras-out", default=os.path.join("gpurun_out", "bench_extras.json"),
+                    help="where the full record (sweeps, ceilings, comparators, e2e, oracle "
+                         "timings) is written; the printed line keeps a summary")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -892,34 +970,20 @@ def main():
             log("bench: oracle on all cores and on one")
             extra("cpu_oracle", lambda: cpu_oracle(wl))
     traffic = traffic_for("matmul.hip")
-    line = {
-        "metric": "invariant matmul TFLOP/s + RMSNorm/attn GB/s (% roofline), bitwise row-invariance",
-        "value": tflops,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) Llama-8B-shaped tensors, random-init weights)",
-        "config": {"workload": "batch-invariant hot path step: RMSNorm [2048,4096] -> "
-                               "matmul [2048,4096]x[4096,14336] -> attention prefill chunk "
-                               "512 @ 4096 + decode B=64 ragged L<=4096, GQA 32/8, d=128, "
-                               "16-token pages",
-                   "M": M, "K": K, "N": N, "decode_batch": B_DEC, "max_kv_len": L_MAX,
-                   "prefill_chunk": PREFILL_CHUNK},
-        "roofline": {"bound": "mfma", "kernel": "bi_matmul_kernel", "achieved": tflops,
-                     "peak": MFMA_BF16_PEAK, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK,
-                     "traffic": traffic},
-        "components": comp,
-        "cpu_baseline": cpu,
-    }
-    line.update(extras)
+    line = headline(args.steps, args.warmup, ms_step, tflops, comp, cpu, traffic, extras,
+                    args.extras_out)
+    if args.extras_out:
+        full = dict(line)
+        full["components"] = comp
+        full.update(extras)
+        try:
+            os.makedirs(os.path.dirname(os.path.abspath(args.extras_out)), exist_ok=True)
+            with open(args.extras_out, "w") as f:
+                json.dump(full, f)
+            log("bench: full record in %s" % args.extras_out)
+        except OSError as e:
+            log("bench: could not write %s: %r" % (args.extras_out, e))
     print(json.dumps(line))
-
 
 if __name__ == "__main__":
     main()
