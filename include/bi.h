@@ -22,8 +22,10 @@
  *
  * CONVENTIONS (all entry points).
  *   - Every tensor argument is a DEVICE pointer to memory owned by the caller.
- *     The library allocates nothing, frees nothing, never synchronises and
- *     keeps no mutable global state; it is reentrant.
+ *     The library allocates nothing, frees nothing and never synchronises.
+ *     Its only mutable global state is bi_attn_decode_noalloc's scratch array
+ *     (and the per-device table of its addresses, filled under a lock); every
+ *     other entry point is reentrant.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
  *     Inputs must stay alive and unmodified until that work completes.
  *   - Host arguments are checked before anything is enqueued.  On any non-OK
@@ -188,6 +190,28 @@ int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, con
                    const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                    void* v_cache, void* out, float* lse, int32_t max_kv_len, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/* bi_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The split-partial records go to a scratch
+ * array of BI_DECODE_SCRATCH_BYTES that the library holds in device memory,
+ * one per GPU it runs on, until the process ends; its address is looked up
+ * (hipGetSymbolAddress) on the first call on each device.  The call allocates
+ * nothing and runs the same kernels as bi_attn_decode, so its outputs are
+ * bitwise those of bi_attn_decode.
+ *   Arguments as bi_attn_decode.  BI_ERR_WORKSPACE_TOO_SMALL (nothing
+ *   enqueued) when bi_attn_workspace_bytes(s, B, max_kv_len) exceeds
+ *   BI_DECODE_SCRATCH_BYTES; BI_ERR_HIP if the scratch address cannot be had.
+ *   Every call on one GPU shares that GPU's array and leaves its records in
+ *   it (each call writes every record it reads first, so nothing needs
+ *   clearing): calls that can overlap on one GPU -- on different streams, or
+ *   from different threads -- race and must be ordered by the caller.
+ *   The debug library does not check the index arrays for this call. */
+#define BI_DECODE_SCRATCH_BYTES (64u << 20)
+int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_new,
+                           const void* v_new, const int32_t* kv_len, const int32_t* block_table,
+                           void* k_cache, void* v_cache, void* out, float* lse,
+                           int32_t max_kv_len, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Non-invariant comparators (the strategies the approach table warns about).

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "BIError", "lib_path", "debug_lib_path", "load", "load_library", "abi_version", "rmsnorm",
     "matmul", "attn_workspace_bytes",
-    "attn_prefill", "attn_decode", "AttnShape", "SPLIT", "PAGE",
+    "attn_prefill", "attn_decode", "attn_decode_noalloc", "DECODE_SCRATCH_BYTES", "AttnShape",
+    "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "matmul_tile", "bix_matmul_splitk", "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
     "qkv_rope", "swiglu_pair",
@@ -29,6 +30,7 @@ __all__ = [
 
 SPLIT = 256
 PAGE = 16
+DECODE_SCRATCH_BYTES = 64 << 20  # BI_DECODE_SCRATCH_BYTES
 DTYPE_BF16, DTYPE_F32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +92,7 @@ def load_library(path: str):
         "bi_attn_workspace_bytes": (sz, [SP, i64, i32]),
         "bi_attn_prefill": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
         "bi_attn_decode": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, i32, P, sz, P]),
+        "bi_attn_decode_noalloc": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, i32, P]),
         "bix_rmsnorm_splitrow": (ctypes.c_int, [P, P, P, P, i64, i64, f32, i32, P, sz, P]),
         "bix_matmul_tile": (ctypes.c_int, [i64, i64, P, P, P]),
         "bix_matmul_workspace_bytes": (sz, [i64, i64, i64, i32]),
@@ -334,6 +337,20 @@ def attn_decode(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, softmax_
         ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_len), _ptr(block_table),
         _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(max_kv_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream()))
+    return (o, lse) if lse is not None else o
+
+
+def attn_decode_noalloc(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, softmax_scale,
+                        max_kv_len: int, out=None, lse=None, with_lse: bool = False):
+    """attn_decode without a workspace: the library keeps the split partials in
+    its own per-GPU scratch array (DECODE_SCRATCH_BYTES) and allocates nothing.
+    Calls that may overlap on one GPU race on that array."""
+    B, nq, nkv, d, P, maxp, o, lse = _decode_args(q, k_new, v_new, kv_len, block_table, k_cache,
+                                                  v_cache, out, lse, with_lse)
+    shape = make_shape(B, nq, nkv, d, maxp, P, softmax_scale)
+    _check("bi_attn_decode_noalloc", load().bi_attn_decode_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kv_len), _ptr(block_table),
+        _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), int(max_kv_len), _stream()))
     return (o, lse) if lse is not None else o
 
 

@@ -1,8 +1,9 @@
 // extern "C" entry points of libbi.so (declared and documented in bi.h).
 //
 // Every entry point checks its host arguments completely before it enqueues
-// anything, then launches on the caller's stream.  Nothing here allocates,
-// synchronises or keeps state.
+// anything, then launches on the caller's stream.  Nothing here allocates or
+// synchronises; the one piece of state is bi_attn_decode_noalloc's scratch
+// array and its per-device address table.
 //
 // Built with BI_DEBUG_CHECKS (libbi_debug.so), the attention entry points
 // also validate the device index arrays before they launch anything: a
@@ -305,6 +306,62 @@ int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, con
     if (e != hipSuccess) return BI_ERR_HIP;
     return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
                                              ns, (float*)workspace, st));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+// ---- decode with no allocation --------------------------------------------
+// The split-partial records of bi_attn_decode_noalloc live in this array: one
+// copy per GPU, held until the process ends.  Host code never passes its name
+// to a kernel (on the host it is only a stand-in for the symbol); it takes the
+// device address that hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) float scratch[BI_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_dev[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call on that
+// device; nullptr if the runtime cannot say.
+float* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return nullptr;
+    scratch_dev[dev] = (float*)p;
+  }
+  return scratch_dev[dev];
+}
+}  // namespace
+
+int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_new,
+                           const void* v_new, const int32_t* kv_len, const int32_t* block_table,
+                           void* k_cache, void* v_cache, void* out, float* lse,
+                           int32_t max_kv_len, void* stream) {
+  try {
+    // the array stands in for the workspace pointer in the shared checks
+    const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
+                               max_kv_len, (void*)k_cache);
+    if (c < 0) return BI_OK;
+    if (c != BI_OK) return c;
+    const int ns = (max_kv_len + bi::kSplit - 1) / bi::kSplit;
+    if (decode_ws_bytes(s, s->num_seqs, ns) > (size_t)BI_DECODE_SCRATCH_BYTES)
+      return BI_ERR_WORKSPACE_TOO_SMALL;
+    if ((int64_t)s->num_seqs * s->num_kv_heads * ns / 4 + 1 > kMaxGridX) return BI_ERR_UNSUPPORTED;
+    float* ws = scratch_for_current_device();
+    if (ws == nullptr) return BI_ERR_HIP;
+    const bi::AttnDims d = dims_of(s);
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
+                                        v_cache, 1, st);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
+                                             ns, ws, st));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }

@@ -129,3 +129,19 @@ def test_attention_validation(lib):
     assert lib.bi_attn_decode(by(s), *dec, 65, _p(), 1 << 30, None) == SHAPE
     assert lib.bi_attn_decode(by(_shape(num_seqs=0)), *dec, 0, None, 0, None) == OK
     assert bi.SPLIT == 256 and bi.PAGE == 16
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode refuses, before any HIP call, a call whose
+    split records would not fit its scratch array."""
+    import invariant_bi_matmul_amd as bi
+    by = ctypes.byref
+    dec = [_p()] * 8 + [None]
+    big = _shape(num_seqs=64, max_pages_per_seq=2048)
+    assert lib.bi_attn_workspace_bytes(by(big), 64, 32768) > bi.DECODE_SCRATCH_BYTES
+    assert lib.bi_attn_decode_noalloc(by(big), *dec, 32768, None) == WS
+    assert lib.bi_attn_decode_noalloc(by(_shape()), *dec, 65, None) == SHAPE
+    assert lib.bi_attn_decode_noalloc(by(_shape(head_dim=96)), *dec, 60, None) == UNSUP
+    assert lib.bi_attn_decode_noalloc(by(_shape()), *([None] + [_p()] * 7 + [None]), 60,
+                                      None) == NULLP
+    assert lib.bi_attn_decode_noalloc(by(_shape(num_seqs=0)), *dec, 0, None) == OK
