@@ -62,6 +62,7 @@ def _load():
     i64, i32, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_double
     lib.bio_abi_version.restype = i32
     lib.bio_bf16_decode.argtypes = [P, P, i64]
+    lib.bio_bf16_encode.argtypes = [P, P, i64]
     lib.bio_rmsnorm_f64.argtypes = [P, P, i64, i64, f64, P, P, i32]
     lib.bio_matmul_f64.argtypes = [P, P, i64, i64, i64, P, i64, P, i32]
     lib.bio_matmul_f64.restype = i32
@@ -94,6 +95,15 @@ def bf16_decode(bits) -> np.ndarray:
     b = _u16(bits)
     out = np.empty(b.shape, dtype=np.float64)
     _load().bio_bf16_decode(_ptr(b), _ptr(out), b.size)
+    return out
+
+
+def bf16_encode(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) of the nearest bf16 to each float64 value,
+    rounded once, ties to even (the oracle's own codec)."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(a.shape, dtype=np.uint16)
+    _load().bio_bf16_encode(_ptr(a), _ptr(out), a.size)
     return out
 
 

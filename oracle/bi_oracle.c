@@ -52,6 +52,33 @@ void bio_bf16_decode(const uint16_t* src, double* dst, int64_t n) {
   for (int64_t i = 0; i < n; ++i) dst[i] = bf16_to_f64(src[i]);
 }
 
+/* The nearest bf16 to an fp64 value, rounded once (ties to even): 8
+ * significant bits within binary32's exponent range, steps of 2^-133 below
+ * 2^-126 (gradual underflow), infinity past the largest finite value.  A NaN
+ * becomes the quiet NaN with its sign.  This is the rounding a bf16 tensor
+ * applies to an exact result; going through fp32 first would round twice. */
+static uint16_t f64_to_bf16(double x) {
+  const uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  if (isnan(x)) return sign | 0x7FC0u;
+  const double ax = fabs(x);
+  if (isinf(ax)) return sign | 0x7F80u;
+  if (ax == 0.0) return sign;
+  int e;
+  frexp(ax, &e); /* ax = f 2^e with 0.5 <= f < 1 */
+  int q = e - 8; /* weight of the 8th significant bit */
+  if (q < -133) q = -133;
+  const double r = ldexp(nearbyint(ldexp(ax, -q)), q); /* scaling is exact */
+  if (r >= ldexp(1.0, 128)) return sign | 0x7F80u;
+  const float f = (float)r; /* exact: at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+void bio_bf16_encode(const double* src, uint16_t* dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = f64_to_bf16(src[i]);
+}
+
 /* ------------------------------------------------------------------------- */
 /* A tiny static work splitter over [0, n): thread t takes a contiguous range. */
 

@@ -226,6 +226,38 @@ def llama_weights(hidden: int, layers: int, n_q: int, n_kv: int, head_dim: int, 
     return out
 
 
+def llama_weights_host(hidden: int, layers: int, n_q: int, n_kv: int, head_dim: int, ffn: int,
+                       vocab: int, seed: int = 0, fp32: bool = False) -> dict:
+    """The same kind of random-init weights drawn on the host (numpy), for
+    stacks small enough to check against the oracle: bf16 bit patterns
+    (uint16) everywhere, or, with ``fp32``, the projections and the lm_head as
+    unrounded float32 values (the embedding table and gammas stay bf16).
+    Projections [in, out] ~ N(0, 1/sqrt(in)), embedding ~ N(0, 1), gammas
+    ~ N(1, 0.1)."""
+    def mat(shape, tag):
+        x = stream(seed, tag).standard_normal(shape, dtype=np.float32) / np.float32(
+            np.sqrt(shape[0]))
+        return x if fp32 else bf16_bits(x)
+
+    def gamma(tag):
+        return normal_bits((hidden,), 1.0, 0.1, seed, tag)
+
+    qd, kvd = n_q * head_dim, n_kv * head_dim
+    out = {"embed": normal_bits((vocab, hidden), 0.0, 1.0, seed, "llama.h.embed"),
+           "final_norm": gamma("llama.h.final_norm"),
+           "lm_head": mat((hidden, vocab), "llama.h.lm_head"),
+           "layers": []}
+    for i in range(layers):
+        t = "llama.h.%d." % i
+        out["layers"].append({
+            "attn_norm": gamma(t + "attn_norm"), "wq": mat((hidden, qd), t + "wq"),
+            "wk": mat((hidden, kvd), t + "wk"), "wv": mat((hidden, kvd), t + "wv"),
+            "wo": mat((qd, hidden), t + "wo"), "mlp_norm": gamma(t + "mlp_norm"),
+            "w_gate": mat((hidden, ffn), t + "w_gate"), "w_up": mat((hidden, ffn), t + "w_up"),
+            "w_down": mat((ffn, hidden), t + "w_down")})
+    return out
+
+
 def token_ids(n: int, vocab: int, seed: int, tag: str) -> List[int]:
     """n random token ids, uniform over the vocabulary."""
     return stream(seed, tag).integers(0, vocab, size=n).tolist()
