@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define BI_ABI_VERSION 2
+#define BI_ABI_VERSION 3
 
 typedef enum {
   BI_OK = 0,
@@ -376,14 +376,27 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
  * packed once). */
 int bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream);
 
-/* Bytes of workspace bi_matmul_ec needs: m * 3k * 2 (the packed A3). */
+/* Bytes of workspace bi_matmul_ec needs for any operand type: m * 3k * 2
+ * (the packed A3; a bf16 a needs only m * 2k * 2). */
 size_t bi_matmul_ec_workspace_bytes(int64_t m, int64_t k);
 
-/* c fp32 [m, n] = the error-compensated product of a fp32 [m, k] and the
- * packed w3 bf16 [3k, n]; k % 64 == 0, n % 8 == 0, 3k <= 2^22.  workspace:
- * device, >= bi_matmul_ec_workspace_bytes(m, k) bytes, receives A3. */
-int bi_matmul_ec(const float* a, const void* w3, float* c, int64_t m, int64_t n, int64_t k,
-                 void* workspace, size_t workspace_bytes, void* stream);
+/* c [m, n] = the error-compensated product of a [m, k] and the packed
+ * w3 bf16 [3k, n].
+ *   a_dtype BI_DTYPE_F32: a fp32 [m, k]; the workspace receives
+ *     A3 = [hi(a) | hi(a) | lo(a)] and c = one bi_matmul of A3 and w3 over
+ *     K' = 3k: the three products above in that order.
+ *   a_dtype BI_DTYPE_BF16: a bf16 [m, k], exactly representable, so lo(a) = 0
+ *     and the third product vanishes; the workspace receives A2 = [a | a] and
+ *     c = one bi_matmul of A2 and the first 2k rows of w3 ([hi(w); lo(w)])
+ *     over K' = 2k.  The sum is the first two products in the same order
+ *     (adding the vanished third product's zeros changes at most the sign
+ *     of a zero sum).
+ *   c_dtype BI_DTYPE_F32 (the fp32 sum) or BI_DTYPE_BF16 (its round to
+ *   nearest even, as bi_matmul's bf16 output).
+ * k % 64 == 0, n % 8 == 0, 3k <= 2^22 (else BI_ERR_UNSUPPORTED).  workspace:
+ * device, >= m * K' * 2 bytes.  Rows are invariant as bi_matmul's are. */
+int bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtype, int64_t m,
+                 int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ __all__ = [
     "matmul", "attn_workspace_bytes",
     "attn_prefill", "attn_decode", "attn_decode_noalloc", "DECODE_SCRATCH_BYTES", "AttnShape",
     "SPLIT", "PAGE",
-    "bix_rmsnorm_splitrow", "matmul_tile", "bix_matmul_splitk", "bix_attn_decode_splitkv",
+    "bix_rmsnorm_splitrow", "matmul_tile", "bix_matmul_splitk",
+    "bix_attn_decode_splitkv",
     "embed", "rope", "swiglu", "add", "argmax", "matmul_ec_pack_w", "matmul_ec",
     "qkv_rope", "swiglu_pair",
     "attn_prefill_i16", "attn_decode_i16", "bix_mfma_loop",
@@ -115,7 +116,8 @@ def load_library(path: str):
                                [SP, P, P, P, P, P, P, P, P, P, P, P, i32, P, sz, P]),
         "bi_matmul_ec_pack_w": (ctypes.c_int, [P, P, i64, i64, P]),
         "bi_matmul_ec_workspace_bytes": (sz, [i64, i64]),
-        "bi_matmul_ec": (ctypes.c_int, [P, P, P, i64, i64, i64, P, sz, P]),
+        "bi_matmul_ec": (ctypes.c_int, [P, ctypes.c_int, P, P, ctypes.c_int, i64, i64, i64, P,
+                                        sz, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -481,22 +483,30 @@ def matmul_ec_pack_w(w: torch.Tensor, out: Optional[torch.Tensor] = None):
 
 
 def matmul_ec(a: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None):
-    """fp32 C = hi(a)hi(w) + hi(a)lo(w) + lo(a)hi(w) for fp32 a [m, k] and a
-    weight packed by ``matmul_ec_pack_w`` (bf16 [3k, n])."""
-    _dev(a, "a", torch.float32)
+              workspace: Optional[torch.Tensor] = None, out_dtype=torch.float32):
+    """C = hi(a)hi(w) + hi(a)lo(w) + lo(a)hi(w) for a [m, k] (fp32, or bf16,
+    whose lo is 0 and whose third product is skipped) and a weight packed by
+    ``matmul_ec_pack_w`` (bf16 [3k, n]); C fp32 or its bf16 rounding."""
+    if not isinstance(a, torch.Tensor) or a.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("a must be a float32 or bfloat16 tensor")
+    _dev(a, "a", a.dtype)
     _dev(w3, "w3", torch.bfloat16)
     if a.dim() != 2 or w3.dim() != 2 or w3.shape[0] != 3 * a.shape[1]:
         raise ValueError("need a [m, k] and w3 [3k, n]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
     m, k = a.shape
     n = w3.shape[1]
-    c = torch.empty(m, n, dtype=torch.float32, device=a.device) if out is None else \
-        _dev(out, "out", torch.float32, (m, n))
+    c = torch.empty(m, n, dtype=out_dtype, device=a.device) if out is None else \
+        _dev(out, "out", out_dtype, (m, n))
     lib = load()
     need = lib.bi_matmul_ec_workspace_bytes(m, k)
     if workspace is None:
         workspace = torch.empty(max(need, 16) // 2 + 8, dtype=torch.bfloat16, device=a.device)
-    _check("bi_matmul_ec", lib.bi_matmul_ec(_ptr(a), _ptr(w3), _ptr(c), m, n, k, _ptr(workspace),
+    a_dt = DTYPE_F32 if a.dtype == torch.float32 else DTYPE_BF16
+    c_dt = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
+    _check("bi_matmul_ec", lib.bi_matmul_ec(_ptr(a), a_dt, _ptr(w3), _ptr(c), c_dt, m, n, k,
+                                            _ptr(workspace),
                                             workspace.numel() * workspace.element_size(),
                                             _stream()))
     return c

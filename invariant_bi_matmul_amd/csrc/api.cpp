@@ -606,24 +606,31 @@ size_t bi_matmul_ec_workspace_bytes(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(3 * k) * 2;
 }
 
-int bi_matmul_ec(const float* a, const void* w3, float* c, int64_t m, int64_t n, int64_t k,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+int bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtype, int64_t m,
+                 int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (m < 0 || n < 0 || k < 0) return BI_ERR_INVALID_SHAPE;
-    if (k > ((int64_t)1 << 22) / 3) return BI_ERR_UNSUPPORTED;
-    // the product itself is bi_matmul over K' = 3k with an fp32 C
-    const int st = check_matmul(workspace, w3, c, BI_DTYPE_F32, m, n, 3 * k);
+    if (a_dtype != BI_DTYPE_BF16 && a_dtype != BI_DTYPE_F32) return BI_ERR_INVALID_SHAPE;
+    if (k > ((int64_t)1 << 22) / 3 || k % bi::kMatmulBK != 0) return BI_ERR_UNSUPPORTED;
+    // the product itself is bi_matmul over K' = 3k (fp32 a: [hi | hi | lo]
+    // against all of w3) or K' = 2k (bf16 a, whose lo is 0: [a | a] against
+    // w3's first 2k rows, [hi; lo])
+    const int64_t kk = (a_dtype == BI_DTYPE_F32 ? 3 : 2) * k;
+    const int st = check_matmul(workspace, w3, c, c_dtype, m, n, kk);
     if (st < 0) return BI_OK;
     if (st != BI_OK) return st;
     if (k > 0 && a == nullptr) return BI_ERR_NULL_POINTER;
     if (!aligned16(a)) return BI_ERR_INVALID_SHAPE;
-    if (workspace_bytes < bi_matmul_ec_workspace_bytes(m, k)) return BI_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < (size_t)m * (size_t)kk * 2) return BI_ERR_WORKSPACE_TOO_SMALL;
     const hipStream_t s = (hipStream_t)stream;
     if (k > 0) {
-      const hipError_t e = bi::launch_ec_pack_a(a, workspace, m, k, s);
+      const hipError_t e = a_dtype == BI_DTYPE_F32
+                               ? bi::launch_ec_pack_a((const float*)a, workspace, m, k, s)
+                               : bi::launch_ec_pack_a_bf16(a, workspace, m, k, s);
       if (e != hipSuccess) return BI_ERR_HIP;
     }
-    return hip_status(bi::launch_matmul(workspace, w3, c, true, m, n, 3 * k, s));
+    return hip_status(
+        bi::launch_matmul(workspace, w3, c, c_dtype == BI_DTYPE_F32, m, n, kk, s));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }

@@ -83,6 +83,7 @@ hipError_t launch_swiglu(const void* gate, const void* up, void* out, int64_t n,
 hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStream_t st);
 hipError_t launch_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, hipStream_t st);
 hipError_t launch_ec_pack_a(const float* a, void* a3, int64_t m, int64_t k, hipStream_t st);
+hipError_t launch_ec_pack_a_bf16(const void* a, void* a2, int64_t m, int64_t k, hipStream_t st);
 hipError_t launch_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, hipStream_t st);
 
 }  // namespace bi

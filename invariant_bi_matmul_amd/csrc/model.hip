@@ -198,6 +198,20 @@ __global__ __launch_bounds__(kElemThreads) void ec_pack_a_kernel(const float* __
     row[2 * k + c] = (uint16_t)lo;
   }
 }
+// a2 [m, 2k] = [a | a] row by row for a bf16 a (whose lo is 0); k % 8 == 0,
+// one thread per 16-byte vector of a.
+__global__ __launch_bounds__(kElemThreads) void ec_pack_a_bf16_kernel(const u32x4* __restrict__ a,
+                                                                      u32x4* __restrict__ a2,
+                                                                      int64_t m, int64_t kv) {
+  const int64_t total = m * kv;
+  for (int64_t i = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kElemThreads) {
+    const int64_t r = i / kv, c = i - r * kv;
+    const u32x4 x = a[i];
+    a2[r * 2 * kv + c] = x;
+    a2[r * 2 * kv + kv + c] = x;
+  }
+}
 // w3 [3k, n] = [hi(w); lo(w); hi(w)] stacked along k.
 __global__ __launch_bounds__(kElemThreads) void ec_pack_w_kernel(const float* __restrict__ w,
                                                                  uint16_t* __restrict__ w3,
@@ -269,6 +283,12 @@ hipError_t launch_add(const void* a, const void* b, void* out, int64_t n, hipStr
 hipError_t launch_ec_pack_a(const float* a, void* a3, int64_t m, int64_t k, hipStream_t st) {
   hipLaunchKernelGGL(ec_pack_a_kernel, dim3(elem_grid(m * k)), dim3(kElemThreads), 0, st, a,
                      (uint16_t*)a3, m, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_ec_pack_a_bf16(const void* a, void* a2, int64_t m, int64_t k, hipStream_t st) {
+  hipLaunchKernelGGL(ec_pack_a_bf16_kernel, dim3(elem_grid(m * (k / 8))), dim3(kElemThreads), 0,
+                     st, (const u32x4*)a, (u32x4*)a2, m, k / 8);
   return hipGetLastError();
 }
 

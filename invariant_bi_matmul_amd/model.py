@@ -33,9 +33,10 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (PAGE, add, argmax, attn_decode, attn_prefill, attn_workspace_bytes,
-               bix_attn_decode_splitkv, bix_matmul_splitk, bix_rmsnorm_splitrow, embed,
-               make_shape, matmul, qkv_rope, rmsnorm, rope, swiglu, swiglu_pair)
+from . import (PAGE, add, argmax, attn_decode, attn_decode_i16, attn_prefill, attn_prefill_i16,
+               attn_workspace_bytes, bix_attn_decode_splitkv, bix_matmul_splitk,
+               bix_rmsnorm_splitrow, embed, make_shape, matmul, matmul_ec, matmul_ec_pack_w,
+               qkv_rope, rmsnorm, rope, swiglu, swiglu_pair)
 
 __all__ = ["LlamaConfig", "LAYER_WEIGHTS", "weight_shapes", "Decoder", "DecodeGraph"]
 
@@ -75,6 +76,9 @@ class _Seq:
     pages: List[int] = field(default_factory=list)
 
 
+PROJECTIONS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
+
+
 class Decoder:
     """Holds the weights and a paged KV cache for up to ``max_tokens`` cached
     positions in total; sequences are added, stepped and released by id.
@@ -89,35 +93,69 @@ class Decoder:
     up as one against [W_gate | W_up] (then ``bi_swiglu_pair``): one launch
     fills the GPU where three small ones each left most of it idle.  Every
     output column is the same dot product in the same k order either way, so
-    the bits are those of the separate projections."""
+    the bits are those of the separate projections.
+
+    ``kv="int16"`` keeps the KV cache as int16 codes with a factor per
+    (token, kv head) (``bi_attn_prefill_i16`` / ``bi_attn_decode_i16``).
+
+    ``mm="ec"`` takes the projection weights (and lm_head) in fp32 and runs
+    every projection as an error-compensated matmul (``bi_matmul_ec``) against
+    the weight packed once as [hi; lo; hi]: the product of the bf16 activation
+    with the fp32 weight, to about 2^-16 of sum |a||w|.  The activations stay
+    bf16 (so lo(a) = 0 and each call takes two products)."""
 
     def __init__(self, cfg: LlamaConfig, weights: dict, max_tokens: int,
                  device: Optional[torch.device] = None, comparator: bool = False,
-                 fuse: bool = True):
+                 fuse: bool = True, kv: str = "bf16", mm: str = "bf16"):
+        if kv not in ("bf16", "int16") or mm not in ("bf16", "ec"):
+            raise ValueError("kv must be 'bf16' or 'int16', mm 'bf16' or 'ec'")
+        if comparator and (kv != "bf16" or mm != "bf16"):
+            raise ValueError("the comparators exist for the bf16 cache and matmul only")
         glob, layer = weight_shapes(cfg)
+        wdt = torch.float32 if mm == "ec" else torch.bfloat16
+
+        def check(name, t, shape):
+            want = wdt if name in PROJECTIONS or name == "lm_head" else torch.bfloat16
+            if tuple(t.shape) != shape or t.dtype != want:
+                raise ValueError("weight %s must be %s %s" % (name, want, shape))
+
         for name, shape in glob.items():
-            if tuple(weights[name].shape) != shape or weights[name].dtype != torch.bfloat16:
-                raise ValueError("weight %s must be bf16 %s" % (name, shape))
+            check(name, weights[name], shape)
         if len(weights["layers"]) != cfg.layers:
             raise ValueError("need %d layers of weights" % cfg.layers)
         for lw in weights["layers"]:
             for name, shape in layer.items():
-                if tuple(lw[name].shape) != shape or lw[name].dtype != torch.bfloat16:
-                    raise ValueError("layer weight %s must be bf16 %s" % (name, shape))
+                check(name, lw[name], shape)
         self.cfg = cfg
         self.w = weights
         self.device = device or weights["embed"].device
         self.fuse = fuse
-        # concatenated projection weights (a one-off copy when the model loads)
-        self.fused = [{"w_qkv": torch.cat([lw["wq"], lw["wk"], lw["wv"]], dim=1).contiguous(),
-                       "w_gu": torch.cat([lw["w_gate"], lw["w_up"]], dim=1).contiguous()}
-                      for lw in weights["layers"]] if fuse else None
+        self.kv, self.mm = kv, mm
+        # the tensors each projection multiplies by: the bf16 weight, or the
+        # packed [hi; lo; hi] of the fp32 one; q|k|v and gate|up concatenated
+        # once when fused
+        prep = matmul_ec_pack_w if mm == "ec" else (lambda t: t)
+        self.proj = []
+        for lw in weights["layers"]:
+            pw = {"wo": prep(lw["wo"]), "w_down": prep(lw["w_down"])}
+            if fuse:
+                pw["w_qkv"] = prep(torch.cat([lw["wq"], lw["wk"], lw["wv"]], dim=1).contiguous())
+                pw["w_gu"] = prep(torch.cat([lw["w_gate"], lw["w_up"]], dim=1).contiguous())
+            else:
+                for name in ("wq", "wk", "wv", "w_gate", "w_up"):
+                    pw[name] = prep(lw[name])
+            self.proj.append(pw)
+        self.lm_head = prep(weights["lm_head"])
         self.num_pages = (max_tokens + PAGE - 1) // PAGE + 1
         cache = (self.num_pages, cfg.n_kv, PAGE, cfg.head_dim)
-        self.kc = [torch.zeros(cache, dtype=torch.bfloat16, device=self.device)
-                   for _ in range(cfg.layers)]
-        self.vc = [torch.zeros(cache, dtype=torch.bfloat16, device=self.device)
-                   for _ in range(cfg.layers)]
+        cdt = torch.int16 if kv == "int16" else torch.bfloat16
+        self.kc = [torch.zeros(cache, dtype=cdt, device=self.device) for _ in range(cfg.layers)]
+        self.vc = [torch.zeros(cache, dtype=cdt, device=self.device) for _ in range(cfg.layers)]
+        if kv == "int16":
+            self.ks = [torch.zeros(cache[:3], dtype=torch.float32, device=self.device)
+                       for _ in range(cfg.layers)]
+            self.vs = [torch.zeros(cache[:3], dtype=torch.float32, device=self.device)
+                       for _ in range(cfg.layers)]
         self.free = list(range(self.num_pages - 1, -1, -1))
         self.seqs: Dict[int, _Seq] = {}
         self.scale = float(torch.tensor(1.0 / math.sqrt(cfg.head_dim), dtype=torch.float32))
@@ -125,6 +163,10 @@ class Decoder:
         if comparator:
             self._norm = lambda x, g: bix_rmsnorm_splitrow(x, g, cfg.eps)
             self._mm = lambda a, w, **kw: bix_matmul_splitk(a, w, **kw)
+        elif mm == "ec":
+            self._norm = lambda x, g: rmsnorm(x, g, cfg.eps)
+            self._mm = lambda a, w3, out_dtype=torch.bfloat16: matmul_ec(a, w3,
+                                                                         out_dtype=out_dtype)
         else:
             self._norm = lambda x, g: rmsnorm(x, g, cfg.eps)
             self._mm = matmul
@@ -195,6 +237,22 @@ class Decoder:
         need = attn_workspace_bytes(shape, B, max_len)
         return torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=self.device)
 
+    def _attend(self, li, q, k, v, cu_q, kv_len, bt, max_new, max_len, ws, decode):
+        """Append k/v to layer li's cache, then attention for q."""
+        kc, vc = self.kc[li], self.vc[li]
+        if self.kv == "int16":
+            ks, vs = self.ks[li], self.vs[li]
+            if decode:
+                return attn_decode_i16(q, k, v, kv_len, bt, kc, vc, ks, vs, self.scale, max_len,
+                                       workspace=ws)
+            return attn_prefill_i16(q, k, v, cu_q, kv_len, bt, kc, vc, ks, vs, self.scale,
+                                    max_new)
+        if decode and self.comparator:
+            return bix_attn_decode_splitkv(q, k, v, kv_len, bt, kc, vc, self.scale, max_len)
+        if decode:
+            return attn_decode(q, k, v, kv_len, bt, kc, vc, self.scale, max_len, workspace=ws)
+        return attn_prefill(q, k, v, cu_q, kv_len, bt, kc, vc, self.scale, max_new)
+
     def _body(self, ids, pos, cu_q, kv_len, bt, last, max_new: int, max_len: int, ws):
         """The stack on device tensors: T = len(ids) tokens of B = len(kv_len)
         sequences; a decode step when max_new == 1.  Only device work, so a
@@ -207,34 +265,63 @@ class Decoder:
 
         x = embed(ids, self.w["embed"])
         for li, lw in enumerate(self.w["layers"]):
+            pw = self.proj[li]
             h = norm(x, lw["attn_norm"])
             if self.fuse:
-                q, k, v = qkv_rope(mm(h, self.fused[li]["w_qkv"]), pos, nq, nkv, cfg.rope_theta)
+                q, k, v = qkv_rope(mm(h, pw["w_qkv"]), pos, nq, nkv, cfg.rope_theta)
             else:
-                q = mm(h, lw["wq"]).view(T, nq, d)
-                k = mm(h, lw["wk"]).view(T, nkv, d)
-                v = mm(h, lw["wv"]).view(T, nkv, d)
+                q = mm(h, pw["wq"]).view(T, nq, d)
+                k = mm(h, pw["wk"]).view(T, nkv, d)
+                v = mm(h, pw["wv"]).view(T, nkv, d)
                 rope(q, k, pos, cfg.rope_theta)
-            if decode and self.comparator:
-                o = bix_attn_decode_splitkv(q, k, v, kv_len, bt, self.kc[li], self.vc[li],
-                                            self.scale, max_len)
-            elif decode:
-                o = attn_decode(q, k, v, kv_len, bt, self.kc[li], self.vc[li], self.scale,
-                                max_len, workspace=ws)
-            else:
-                o = attn_prefill(q, k, v, cu_q, kv_len, bt, self.kc[li], self.vc[li], self.scale,
-                                 max_new)
-            add(x, mm(o.view(T, nq * d), lw["wo"]), out=x)
+            o = self._attend(li, q, k, v, cu_q, kv_len, bt, max_new, max_len, ws, decode)
+            add(x, mm(o.view(T, nq * d), pw["wo"]), out=x)
             h = norm(x, lw["mlp_norm"])
             if self.fuse:
-                g = swiglu_pair(mm(h, self.fused[li]["w_gu"]))
+                g = swiglu_pair(mm(h, pw["w_gu"]))
             else:
-                g = mm(h, lw["w_gate"])
-                swiglu(g, mm(h, lw["w_up"]), out=g)
-            add(x, mm(g, lw["w_down"]), out=x)
+                g = mm(h, pw["w_gate"])
+                swiglu(g, mm(h, pw["w_up"]), out=g)
+            add(x, mm(g, pw["w_down"]), out=x)
         xl = embed(last, x)  # the last new token of each sequence (a row gather)
-        logits = mm(norm(xl, self.w["final_norm"]), self.w["lm_head"], out_dtype=torch.float32)
+        logits = mm(norm(xl, self.w["final_norm"]), self.lm_head, out_dtype=torch.float32)
         return logits, argmax(logits)
+
+    # ---- the cache on the host (suspend and resume) ----------------------------
+    def export_state(self, sids: Sequence[int]) -> dict:
+        """Copy the named sequences' cached keys and values (every layer, their
+        pages only, in position order) and their lengths to host memory."""
+        out = {"lengths": {}, "layers": []}
+        for sid in sids:
+            out["lengths"][sid] = self.seqs[sid].length
+        for li in range(self.cfg.layers):
+            per = {}
+            for sid in sids:
+                pg = torch.tensor(self.seqs[sid].pages, dtype=torch.long, device=self.device)
+                arrs = [self.kc[li], self.vc[li]]
+                if self.kv == "int16":
+                    arrs += [self.ks[li], self.vs[li]]
+                per[sid] = [a.index_select(0, pg).cpu() for a in arrs]
+            out["layers"].append(per)
+        return out
+
+    def import_state(self, state: dict):
+        """Re-create sequences from ``export_state``'s copy: each gets fresh
+        pages from the pool (wherever they fall) holding the same keys and
+        values at the same positions."""
+        for sid, L in state["lengths"].items():
+            self.add_sequence(sid)
+            s = self.seqs[sid]
+            self._reserve(s, L)
+            s.length = L
+        for li, per in enumerate(state["layers"]):
+            arrs = [self.kc[li], self.vc[li]]
+            if self.kv == "int16":
+                arrs += [self.ks[li], self.vs[li]]
+            for sid, saved in per.items():
+                pg = torch.tensor(self.seqs[sid].pages, dtype=torch.long, device=self.device)
+                for a, host in zip(arrs, saved):
+                    a.index_copy_(0, pg, host.to(self.device))
 
     def decode_graph(self, sids: Sequence[int], max_len: int) -> "DecodeGraph":
         """Decode steps of the sequences ``sids`` (in this order) until any
