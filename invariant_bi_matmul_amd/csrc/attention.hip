@@ -881,7 +881,9 @@ void bi_attn_decode_partial_kernel(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int bi = c * 64 + lane;
-      const int ns = bi < B ? (kv_len[bi] + kSplit - 1) / kSplit : 0;
+      // at most smax splits whatever kv_len holds: a length past the call's
+      // bound never addresses records beyond its sequence's
+      const int ns = bi < B ? min(smax, (kv_len[bi] + kSplit - 1) / kSplit) : 0;
       int x = ns;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -995,46 +997,82 @@ void bi_attn_decode_partial_kernel(
 }
 
 // Fold the splits of one (sequence, q head) left in ascending order.
-// Thread d owns output dim d.  Partials are read in batches of 32 splits whose
-// loads are all issued before the batch is folded (the fold itself is the
-// same sequential left fold).
-template <int D>
+// The left fold  m' = max(m, m_s), a = 2^(m - m'), b = 2^(m_s - m'),
+// l = fma(l, a, l_s b), o = fma(o, a, o_s b)  splits into what depends on the
+// running state only through the max and what carries values from step to
+// step.  The running max after split s is the prefix max M_s of the split
+// maxima (fmaxf is exact, so any grouping gives the same M_s), and each step's
+// coefficients a_s = 2^(M_{s-1} - M_s), b_s = 2^(m_s - M_s) follow from it
+// alone: they are computed for a whole chunk of D splits at once (thread t:
+// split s0 + t; prefix max by a wave scan, then across waves).  What stays
+// sequential is the fma chain of l and of each output dim (thread d owns dim
+// d), over the same values in the same order as the fold step by step, so the
+// bits are those of fold_coef / fold_apply applied in turn.  A chunk (CH <= D
+// splits: 32 when every sequence fits in 33 splits, else D) has all its
+// records requested before its chain starts.
+template <int D, int CH>
 __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restrict__ ws,
                                                             const int32_t* __restrict__ kv_len,
                                                             uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, int nq,
                                                             int smax, int split_len) {
-  constexpr int BATCH = 32;
+  static_assert(CH <= D, "one split per thread in the scan");
+  constexpr int F = PartialRec<D>::FLOATS, NW = D / kWave;
+  __shared__ float sa[CH], sb[CH], sl[CH], wmax[NW], mlast;
   const int64_t bh = blockIdx.x;
   const int b = (int)(bh / nq);
-  const int d = threadIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int L = kv_len[b];
   const int ns = min(smax, (L + split_len - 1) / split_len);
-  const float* rec = ws + bh * smax * PartialRec<D>::FLOATS;
-  float m = rec[D], l = rec[D + 1], o = rec[d];
-  for (int s0 = 1; s0 < ns; s0 += BATCH) {
-    float pm[BATCH], pl[BATCH], po[BATCH];
+  const float* rec = ws + bh * smax * F;
+  float M = rec[D], l = rec[D + 1], o = rec[t];  // split 0 is the initial state
+  for (int s0 = 1; s0 < ns; s0 += CH) {
+    const int n = min(CH, ns - s0);  // splits s0 .. s0+n-1 in this chunk
+    // every record value of the thread's dim in the chunk, requested at once
+    float po[CH];
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int s = min(s0 + j, ns - 1);
-      const float* rs = rec + (int64_t)s * PartialRec<D>::FLOATS;
-      pm[j] = rs[D];
-      pl[j] = rs[D + 1];
-      po[j] = rs[d];
-    }
-    // the steps past the last split keep the state by a select, not a
-    // branch, so that the batch is one block the scheduler can interleave
+    for (int j = 0; j < CH; ++j)
+      if (j < n) po[j] = rec[(int64_t)(s0 + j) * F + t];
+    // thread t: split s0+t's max; prefix max over the chunk, carried in
+    const float* rt = rec + (int64_t)(s0 + min(t, n - 1)) * F;
+    const float ms = t < n ? rt[D] : -INFINITY;
+    float pm = ms;
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const bool ok = s0 + j < ns;
-      const FoldCoef f = fold_coef(m, pm[j]);
-      l = ok ? fold_apply(l, pl[j], f) : l;
-      o = ok ? fold_apply(o, po[j], f) : o;
-      m = ok ? f.m : m;
+    for (int k = 1; k < kWave; k <<= 1) {
+      const float y = __shfl_up(pm, k);
+      if (lane >= k) pm = fmaxf(pm, y);
     }
+    if (lane == kWave - 1) wmax[wave] = pm;
+    __syncthreads();
+    float before = M;  // the running max before this wave's first split
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) before = fmaxf(before, wmax[w]);
+    pm = fmaxf(pm, before);                  // M_{s0+t}
+    float prev = __shfl_up(pm, 1);           // M_{s0+t-1}
+    if (lane == 0) prev = before;
+    if (t < n) {
+      const FoldCoef f = fold_coef(prev, ms);
+      sa[t] = f.a;
+      sb[t] = f.b;
+      sl[t] = rt[D + 1];
+    }
+    if (t == n - 1) mlast = pm;
+    __syncthreads();
+    // the chains, in split order
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (j < n) {
+        const FoldCoef f{sa[j], sb[j], 0.0f};
+        o = fold_apply(o, po[j], f);
+        l = fold_apply(l, sl[j], f);
+      }
+    }
+    M = mlast;
+    __syncthreads();  // every read of this chunk's arrays is done
   }
-  out[bh * D + d] = (uint16_t)f32_to_bf16(o / l);
-  if (lse != nullptr && d == 0) lse[bh] = lse_of(m, l);
+  out[bh * D + t] = (uint16_t)f32_to_bf16(o / l);
+  if (lse != nullptr && t == 0) lse[bh] = lse_of(M, l);
 }
 
 // ---- prefill -----------------------------------------------------------------
@@ -1446,15 +1484,23 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* k
       BI_DECODE(128, true);
     else
       BI_DECODE(128, false);
-    hipLaunchKernelGGL(bi_attn_combine_kernel<128>, grid2, dim3(128), 0, st, (const float*)ws,
-                       kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
+    if (max_splits <= 33)
+      hipLaunchKernelGGL((bi_attn_combine_kernel<128, 32>), grid2, dim3(128), 0, st,
+                         (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
+    else
+      hipLaunchKernelGGL((bi_attn_combine_kernel<128, 128>), grid2, dim3(128), 0, st,
+                         (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
   } else {
     if (q16)
       BI_DECODE(64, true);
     else
       BI_DECODE(64, false);
-    hipLaunchKernelGGL(bi_attn_combine_kernel<64>, grid2, dim3(64), 0, st, (const float*)ws,
-                       kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
+    if (max_splits <= 33)
+      hipLaunchKernelGGL((bi_attn_combine_kernel<64, 32>), grid2, dim3(64), 0, st,
+                         (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
+    else
+      hipLaunchKernelGGL((bi_attn_combine_kernel<64, 64>), grid2, dim3(64), 0, st,
+                         (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
   }
 #undef BI_DECODE
   return hipGetLastError();
@@ -1486,14 +1532,14 @@ hipError_t launch_attn_decode_splitkv(const AttnDims& s, const void* q, const in
     hipLaunchKernelGGL(bix_attn_decode_splitkv_kernel<128>, grid1, dim3(256), 0, st,
                        (const uint16_t*)q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
                        ws, s.B, s.nq, s.nkv, s.max_pages, nsplit, split_len, c2);
-    hipLaunchKernelGGL(bi_attn_combine_kernel<128>, grid2, dim3(128), 0, st, (const float*)ws,
-                       kv_len, (uint16_t*)out, lse, s.nq, nsplit, split_len);
+    hipLaunchKernelGGL((bi_attn_combine_kernel<128, 128>), grid2, dim3(128), 0, st,
+                       (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, nsplit, split_len);
   } else {
     hipLaunchKernelGGL(bix_attn_decode_splitkv_kernel<64>, grid1, dim3(256), 0, st,
                        (const uint16_t*)q, kv_len, bt, (const uint16_t*)kc, (const uint16_t*)vc,
                        ws, s.B, s.nq, s.nkv, s.max_pages, nsplit, split_len, c2);
-    hipLaunchKernelGGL(bi_attn_combine_kernel<64>, grid2, dim3(64), 0, st, (const float*)ws,
-                       kv_len, (uint16_t*)out, lse, s.nq, nsplit, split_len);
+    hipLaunchKernelGGL((bi_attn_combine_kernel<64, 64>), grid2, dim3(64), 0, st,
+                       (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, nsplit, split_len);
   }
   return hipGetLastError();
 }

@@ -155,6 +155,53 @@ def test_long_context_32768(orc):
     assert np.array_equal(tail.out[0][L - 2:], one.out[0][L - 2:])
 
 
+def _chunks_then_decode(run, lens, chunk, tail):
+    """Prefill every sequence to len - tail in calls of `chunk` tokens per
+    sequence (all sequences with tokens left in each call), then `tail`
+    decode steps of the whole batch."""
+    B = len(lens)
+    while True:
+        items = [(b, min(chunk, lens[b] - tail - run.cur[b])) for b in range(B)
+                 if run.cur[b] < lens[b] - tail]
+        if not items:
+            break
+        run.prefill(items)
+    for _ in range(tail):
+        run.decode(list(range(B)))
+
+
+def test_long_context_32768_in_512_token_chunks(orc):
+    """The attention workload's chunking at L = 32768: 512-token chunks, then
+    decode steps, equal one-shot prefill bit for bit (GQA 32/8, d=128)."""
+    L = 32768
+    prob = _gqa([L], seed=9)
+    one = PagedRun(prob, page_seed=5)
+    one.prefill([(0, L)])
+    ch = PagedRun(prob, page_seed=11)
+    _chunks_then_decode(ch, [L], 512, 4)
+    assert np.array_equal(ch.out[0], one.out[0])
+    assert np.array_equal(ch.lse[0].view(np.uint32), one.lse[0].view(np.uint32))
+    _parity(orc, prob, ch, [(0, p) for p in (511, 512, 16383, 32764, 32767)])
+
+
+def test_ragged_batch_up_to_32768_in_512_token_chunks(orc):
+    """A ragged batch whose longest sequence holds 32768 positions (the
+    others 9000 and 20001): 512-token chunks of the whole batch per call,
+    then decode steps, equal each sequence's one-shot prefill bit for bit.
+    8 q heads over 2 kv heads (group 4, d=128) keep the host inputs small."""
+    lens = [9000, 32768, 20001]
+    prob = synth.attn_problem(lens, n_q=8, n_kv=2, d=128, seed=13,
+                              tags=["rg%d" % i for i in range(3)])
+    one = PagedRun(prob, page_seed=3)
+    one.prefill([(b, L) for b, L in enumerate(lens)])
+    ch = PagedRun(prob, page_seed=4)
+    _chunks_then_decode(ch, lens, 512, 3)
+    for b in range(3):
+        assert np.array_equal(ch.out[b], one.out[b]), b
+        assert np.array_equal(ch.lse[b].view(np.uint32), one.lse[b].view(np.uint32)), b
+    _parity(orc, prob, ch, [(0, 8999), (1, 32767), (1, 12345), (2, 20000), (2, 256)])
+
+
 def test_pins_position0_and_uniform(orc):
     d, nq, nkv = 128, 32, 8
     L = 300
