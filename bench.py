@@ -724,18 +724,20 @@ def calibrate_copy(nbytes=1 << 30):
     print(json.dumps({"copy_bytes_each_way": nbytes, "launches": 3}))
 
 
-def e2e_llama8b(steps: int = 128):
+def e2e_llama8b(steps: int = 128, calls: int = 30):
     """The whole stack end to end: a Llama-3-8B-shaped dense decoder (32 layers,
     hidden 4096, GQA 32/8, SwiGLU 14336, vocab 128256, random-init weights) run
     on the library's kernels.  A 256-token random prompt is decoded greedily
     for ``steps`` tokens alone and among 63 other random prompts (lengths
-    U{64..512}); its tokens and logits are compared bit for bit.  The same is
-    done with the non-invariant comparator kernels.  ``unique_outputs`` counts
-    the distinct token sequences the probe gets over batches of 1, 4, 16 and 64
-    (the news.hada.io page's GPT-4 experiment counted unique outputs over
-    repeated calls).  Decode steps are replayed from a captured HIP graph (about
-    400 library calls per step); the prefill calls are eager.  Wall times
-    include the prefill and the host's per-step bookkeeping."""
+    U{64..512}); its tokens and logits are compared bit for bit.  Then, as the
+    news.hada.io page's GPT-4 experiment counted the distinct outputs of 30
+    repeated calls at temperature 0 with 128 tokens, the probe is decoded in
+    ``calls`` calls, each among a different random set of companions (batch
+    sizes drawn from 1..64, the probe at a random place), and its distinct
+    token sequences are counted.  The same is done with the non-invariant
+    comparator kernels.  Decode steps are replayed from a captured HIP graph
+    (about 400 library calls per step); the prefill calls are eager.  Wall
+    times include the prefill and the host's per-step bookkeeping."""
     import torch
     import synth
     from invariant_bi_matmul_amd.model import Decoder, LlamaConfig
@@ -746,6 +748,13 @@ def e2e_llama8b(steps: int = 128):
     lens = synth.stream(0, "e2e.lens").integers(64, 513, size=63).tolist()
     others = [(i + 1, synth.token_ids(L, cfg.vocab, 0, "e2e.c%d" % i)) for i, L in enumerate(lens)]
     cap = 64 * (512 + steps) + 64
+    rng = synth.stream(0, "e2e.calls")
+    plan = []
+    for _ in range(calls):
+        n = int(rng.choice([1, 2, 4, 8, 16, 32, 48, 64]))
+        comp = [others[i] for i in rng.permutation(63)[:n - 1]]
+        at = int(rng.integers(0, n))
+        plan.append(comp[:at] + [(0, probe)] + comp[at:])
 
     def batch_of(n):
         b = dict(others[:(n - 1) // 2])
@@ -759,7 +768,8 @@ def e2e_llama8b(steps: int = 128):
     out = {"config": {"layers": cfg.layers, "hidden": cfg.hidden, "n_q": cfg.n_q,
                       "n_kv": cfg.n_kv, "ffn": cfg.ffn, "vocab": cfg.vocab,
                       "rope_theta": cfg.rope_theta, "prompt": 256, "companions": 63,
-                      "steps": steps}}
+                      "steps": steps, "calls": calls,
+                      "call_batch_sizes": [len(b) for b in plan]}}
     for name, comp in (("invariant", False), ("comparator", True)):
         dec = Decoder(cfg, w, max_tokens=cap, comparator=comp)
         torch.cuda.synchronize()
@@ -772,9 +782,10 @@ def e2e_llama8b(steps: int = 128):
         t2 = time.perf_counter()
         same = [torch.equal(x.view(torch.int32), y.view(torch.int32))
                 for x, y in zip(a_log[0], b_log[0])]
-        uniq = {tuple(a_tok[0]), tuple(b_tok[0])}
-        for n in (4, 16):
-            uniq.add(tuple(dec.generate(batch_of(n), steps)[0][0]))
+        uniq = set()
+        for batch in plan:
+            uniq.add(tuple(dec.generate(dict(batch), steps)[0][0]))
+        torch.cuda.synchronize()
         out[name] = {"alone_s": t1 - t0, "batched64_s": t2 - t1,
                      "batched64_tokens_per_s": 64 * steps / (t2 - t1),
                      "tokens_equal": a_tok[0] == b_tok[0],
@@ -782,7 +793,8 @@ def e2e_llama8b(steps: int = 128):
                      "first_differing_token": differs(a_tok[0], b_tok[0]),
                      "first_differing_logits_step": next((i for i, s in enumerate(same)
                                                           if not s), None),
-                     "unique_outputs_over_batches_1_4_16_64": len(uniq)}
+                     "unique_outputs_over_%d_calls" % calls: len(uniq),
+                     "calls_s": time.perf_counter() - t2}
         del dec, a_log, b_log
         torch.cuda.empty_cache()
     return out
@@ -879,6 +891,9 @@ def main():
                     help="run only the size sweeps or the ceilings and print them")
     ap.add_argument("--sweep-parts", default="matmul,rmsnorm,decode,prefill",
                     help="with --only sweeps: which sweeps, comma-separated")
+    ap.add_argument("--stage", choices=("rmsnorm", "matmul", "prefill", "decode"),
+                    help="run only this stage of the step, --warmup + --steps times (for "
+                         "profiler passes), and print its average time")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--extras-out", default=os.path.join("gpurun_out", "bench_extras.json"),
                     help="where the full record (sweeps, ceilings, comparators, e2e, oracle "
@@ -902,6 +917,11 @@ def main():
     wl = Workload()
     if args.only == "sweeps":
         print(json.dumps({"sweeps": sweeps(wl, tuple(args.sweep_parts.split(",")))}))
+        return
+    if args.stage:
+        fn = getattr(wl, args.stage)
+        ms = time_call(fn, reps=args.steps, warmup=args.warmup)
+        print(json.dumps({"stage": args.stage, "calls": args.steps, "ms": ms}))
         return
     log("bench: warmup %d, timing %d steps" % (args.warmup, args.steps))
     torch.cuda.synchronize()
