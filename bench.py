@@ -213,25 +213,64 @@ def invariance_check(wl):
     return res
 
 
+# The decoder stack's projections (Llama-8B shape, fused as the stack runs
+# them): (K, N) per layer, and the lm_head once per token.
+STACK_MATMULS = {"qkv": (4096, 6144), "o": (4096, 4096), "gate_up": (4096, 28672),
+                 "down": (14336, 4096), "lm_head": (4096, 128256)}
+
+
 def comparators(wl):
-    """Invariant kernel vs its non-invariant comparator on the same inputs (ms)."""
+    """Invariant kernel vs its non-invariant comparator on the same inputs (ms),
+    warm.  Matmul: the decoder stack's projection shapes at M = 1, 16, 64 (the
+    decode batches) and the step's 2048 x 4096 x 14336, each beside split-K
+    (bi_matmul's tile with k split to fill idle CUs) and the vendor GEMM
+    (torch.matmul, not batch-invariant); `stack_token_ms` adds up one decode
+    token's projections (32 layers + lm_head) for each kernel."""
     import torch
-    bi = wl.bi
+    bi, synth, dev = wl.bi, wl.synth, wl.dev
     out = {}
-    for m in (1, 16, 256, 2048):
-        a = wl.y[:m].contiguous()
-        ws = torch.empty(max(1, wl.bi.load().bix_matmul_workspace_bytes(m, N, K, 0)) // 4 + 4,
-                         dtype=torch.float32, device=wl.dev)
-        ti = time_call(lambda: bi.matmul(a, wl.w, out=wl.c[:m]))
-        tc = time_call(lambda: bi.bix_matmul_splitk(a, wl.w, out=wl.c[:m], workspace=ws))
-        out["matmul_M%d_N%d" % (m, N)] = {"invariant_ms": ti, "splitk_ms": tc,
-                                          "invariant_over_splitk": ti / tc}
+    lib = bi.load()
+    a_big = synth.device_normal_bf16((2048, 14336), 0.0, 1.0, 0, "cmp.a", dev)
+    shapes = [("step_2048x4096x14336", 2048, 4096, 14336)]
+    for m in (1, 16, 64):
+        for name, (k, n) in STACK_MATMULS.items():
+            shapes.append(("%s_M%d" % (name, m), m, k, n))
+    most = max(lib.bix_matmul_workspace_bytes(m, n, k, 0) for _, m, k, n in shapes)
+    ws = torch.empty(most // 4 + 16, dtype=torch.float32, device=dev)
+    ws_cache = {}
+    per_token = {m: {"invariant": 0.0, "splitk": 0.0, "vendor": 0.0} for m in (1, 16, 64)}
+    for label, m, k, n in shapes:
+        if (k, n) not in ws_cache:
+            ws_cache[(k, n)] = (wl.w if (k, n) == (K, N) else
+                                synth.device_normal_bf16((k, n), 0.0, k ** -0.5, 0,
+                                                         "cmp.w%dx%d" % (k, n), dev))
+        w = ws_cache[(k, n)]
+        a = a_big[:m, :k].contiguous()
+        c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        need = lib.bix_matmul_workspace_bytes(m, n, k, 0)
+        ti = time_call(lambda: bi.matmul(a, w, out=c))
+        tc = time_call(lambda: bi.bix_matmul_splitk(a, w, out=c, workspace=ws[:need // 4 + 4]))
+        tv = time_call(lambda: torch.matmul(a, w, out=c))
+        splits = max(1, need // (4 * m * n))
+        out["matmul_" + label] = {"invariant_ms": ti, "splitk_ms": tc, "vendor_ms": tv,
+                                  "splitk_slices": splits,
+                                  "invariant_over_splitk": ti / tc,
+                                  "invariant_over_vendor": ti / tv}
+        if label != shapes[0][0]:
+            reps = 1 if label.startswith("lm_head") else 32
+            for kind, t in (("invariant", ti), ("splitk", tc), ("vendor", tv)):
+                per_token[m][kind] += reps * t
+    for m, r in per_token.items():
+        r["invariant_over_splitk"] = r["invariant"] / r["splitk"]
+        r["invariant_over_vendor"] = r["invariant"] / r["vendor"]
+    out["stack_token_ms"] = per_token
+    del ws, a_big, ws_cache
     for r in (1, 16, 2048):
         xr = wl.x[:r].contiguous()
-        ws = torch.empty(r * 64, dtype=torch.float32, device=wl.dev)
+        wsr = torch.empty(r * 64, dtype=torch.float32, device=dev)
         yr = torch.empty_like(xr)
         ti = time_call(lambda: bi.rmsnorm(xr, wl.g, wl.eps, out=yr))
-        tc = time_call(lambda: bi.bix_rmsnorm_splitrow(xr, wl.g, wl.eps, out=yr, workspace=ws))
+        tc = time_call(lambda: bi.bix_rmsnorm_splitrow(xr, wl.g, wl.eps, out=yr, workspace=wsr))
         out["rmsnorm_rows%d" % r] = {"invariant_ms": ti, "splitrow_ms": tc,
                                      "invariant_over_splitrow": ti / tc}
     for bsz in (1, 8, 64):
@@ -239,12 +278,13 @@ def comparators(wl):
         args = (wl.q_dec[sl].contiguous(), wl.k_dec[sl].contiguous(), wl.v_dec[sl].contiguous(),
                 wl.kvl_dec[sl].contiguous(), wl.bt_dec[sl].contiguous(), wl.kc, wl.vc, wl.scale,
                 L_MAX)
-        o = torch.empty(bsz, NQ, D, dtype=torch.bfloat16, device=wl.dev)
+        o = torch.empty(bsz, NQ, D, dtype=torch.bfloat16, device=dev)
         ti = time_call(lambda: bi.attn_decode(*args, out=o))
         tc = time_call(lambda: bi.bix_attn_decode_splitkv(*args, out=o))
         out["decode_B%d_L%d" % (bsz, L_MAX)] = {"invariant_ms": ti, "splitkv_ms": tc,
                                                 "invariant_over_splitkv": ti / tc}
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return out
 
 
@@ -826,9 +866,15 @@ def _summary(extras):
         out["invariance_bitwise"] = inv
     coi = extras.get("cost_of_invariance")
     if isinstance(coi, dict) and "error" not in coi:
+        keep = ("matmul_step", "rmsnorm", "decode")
         out["cost_of_invariance"] = {
             k: {r: x for r, x in v.items() if r.startswith("invariant_over")}
-            for k, v in coi.items() if isinstance(v, dict)}
+            for k, v in coi.items() if isinstance(v, dict) and k.startswith(keep)}
+        tok = coi.get("stack_token_ms")
+        if isinstance(tok, dict):
+            out["cost_of_invariance"]["stack_token_matmuls"] = {
+                "M%s" % m: {r: x for r, x in v.items() if r.startswith("invariant_over")}
+                for m, v in tok.items()}
     e2e = extras.get("e2e_llama8b")
     if isinstance(e2e, dict) and "error" not in e2e:
         keep = ("tokens_equal", "logits_bitwise_equal", "batched64_tokens_per_s", "alone_s")

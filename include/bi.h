@@ -184,6 +184,12 @@ int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, co
  *   q bf16 [B, n_q, d]; k_new, v_new bf16 [B, n_kv, d]; out bf16 [B, n_q, d];
  *   lse fp32 [B, n_q] or NULL.
  *   max_kv_len (host) >= every kv_len[b] (after the append), sizes the grid.
+ * Requires 1 <= kv_len[b] <= max_kv_len (trusted).  The append runs inside
+ * the split pass, in the one wave that reads the split holding that position
+ * for that kv head: it writes the rows and then reads them from the pool like
+ * every other row, so outputs and pool contents are those of an append
+ * followed by attention.  A length beyond max_kv_len leaves its row
+ * unwritten and its outputs undefined. */
  *   workspace: device, >= bi_attn_workspace_bytes(s, B, max_kv_len) bytes,
  *   contents on entry ignored, scratch for the per-split partials. */
 int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
@@ -226,9 +232,12 @@ int bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd,
                          int64_t hidden, float eps, int32_t chunks, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* bix_matmul_splitk: the k range is split into `split_k` slices (split_k <= 0:
- * chosen from m, n so that the grid fills the GPU), fp32 partials are summed
- * in slice order by a second kernel.  workspace >= bix_matmul_workspace_bytes. */
+/* bix_matmul_splitk: bi_matmul's tile for the shape, with the k range split
+ * into `split_k` slices (split_k <= 0: enough slices for one workgroup per CU
+ * over that tile's grid, at most 16 -- so more slices for smaller m); fp32
+ * partials are summed in slice order by a second kernel.  With one slice it
+ * is bi_matmul (no workspace is touched).  workspace >=
+ * bix_matmul_workspace_bytes. */
 size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
 int bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
                       int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,

@@ -301,11 +301,9 @@ int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, con
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
     BI_CHECK_TABLES(s, kv_len, nullptr, block_table, max_kv_len, 1, 0, st);
-    hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
-                                        v_cache, 1, st);
-    if (e != hipSuccess) return BI_ERR_HIP;
-    return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
-                                             ns, (float*)workspace, st));
+    // the decode kernel appends k_new / v_new itself
+    return hip_status(bi::launch_attn_decode(d, q, k_new, v_new, kv_len, block_table, k_cache,
+                                             v_cache, out, lse, ns, (float*)workspace, st));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }
@@ -357,11 +355,8 @@ int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_
     if (ws == nullptr) return BI_ERR_HIP;
     const bi::AttnDims d = dims_of(s);
     const hipStream_t st = (hipStream_t)stream;
-    hipError_t e = bi::launch_kv_append(d, k_new, v_new, nullptr, kv_len, block_table, k_cache,
-                                        v_cache, 1, st);
-    if (e != hipSuccess) return BI_ERR_HIP;
-    return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
-                                             ns, ws, st));
+    return hip_status(bi::launch_attn_decode(d, q, k_new, v_new, kv_len, block_table, k_cache,
+                                             v_cache, out, lse, ns, ws, st));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }
@@ -580,8 +575,9 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
     hipError_t e = bi::launch_kv_append_i16(d, k_new, v_new, nullptr, kv_len, block_table,
                                             k_cache, v_cache, k_scale, v_scale, 1, st);
     if (e != hipSuccess) return BI_ERR_HIP;
-    return hip_status(bi::launch_attn_decode(d, q, kv_len, block_table, k_cache, v_cache, out, lse,
-                                             ns, (float*)workspace, st, k_scale, v_scale));
+    return hip_status(bi::launch_attn_decode(d, q, nullptr, nullptr, kv_len, block_table, k_cache,
+                                             v_cache, out, lse, ns, (float*)workspace, st,
+                                             k_scale, v_scale));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }

@@ -684,8 +684,12 @@ struct StreamSrc {
   static constexpr int SLOT = 32 * KV<D>::ROWB;      // bytes per chunk
   static constexpr int LOADS = SLOT / 1024;          // 1 KiB loads per chunk
   static constexpr int AHEAD = RING - 1;             // chunks in flight
-  // q copy of the next unit (and, int16 cache, its key and value factors)
-  static constexpr int QLOADS = 16 * KV<D>::ROWB / 1024 + (Q16_ ? 2 : 0);
+  // bf16 cache: the call's new key and value rows are written by the wave
+  // that reads them (append)
+  static constexpr bool APPEND = !Q16_;
+  // q copy of the next unit, then (int16 cache) its key and value factors or
+  // (bf16 cache) its sequence's new key and value rows
+  static constexpr int QLOADS = 16 * KV<D>::ROWB / 1024 + 2;
   static constexpr int STORES = PartialRec<D>::STORES;    // previous unit's record
   static_assert(16 % RING == 0, "slots repeat every split");
   static_assert(LOADS * (AHEAD - 1) + STORES + QLOADS <= 63, "vmcnt range");
@@ -699,6 +703,30 @@ struct StreamSrc {
   bool first;  // the wave's first unit: no record stores precede its chunks
   // int16 cache: LDS addresses of the current unit's 256 key / value factors
   uint32_t kscl = 0, vscl = 0;
+  // bf16 cache: LDS address of the next unit's staged new rows (key row at
+  // +0, value row at +1024)
+  uint32_t nstage = 0;
+
+  // A unit that holds its sequence's last position writes that position's
+  // key and value rows (staged in LDS at `stage`) into the pool before any
+  // chunk of the unit is requested.  Its wave is the only reader of those
+  // rows in the call, and its later loads see the stores: a wave's memory
+  // operations on one address take effect in program order, and lanes of
+  // one wave share the same vector L1.  Positions past the last re-read the
+  // last row (dma_block), so every row loaded has been written.  The page
+  // of the last position is pg[15] for every split that holds it.
+  __device__ __forceinline__ void append(const DecodeUnit<D>& un, uint32_t stage) const {
+    if (un.last - un.key0 >= kSplit) return;  // wave-uniform
+    constexpr int CPR = KV<D>::CPR;
+    const int lane = threadIdx.x & (kWave - 1), j = lane % CPR;
+    const bool isv = lane >= CPR;
+    const u32x4 x = *(lds_u32x4*)(uintptr_t)(stage + (isv ? 1024u : 0u) + 16u * (uint32_t)j);
+    if (lane < 2 * CPR) {
+      uint16_t* pool = const_cast<uint16_t*>(isv ? vc : kc);
+      const int64_t row = (((int64_t)un.sp.pg[15] * nkv + un.g) << 4) + (un.last & 15);
+      *(u32x4*)(pool + row * D + 8 * j) = x;
+    }
+  }
   __device__ __forceinline__ void factors(uint32_t base, int C, float (&f)[8]) const {
     const int q = (threadIdx.x & (kWave - 1)) >> 4;
     const uint32_t a = base + (uint32_t)(32 * C + 8 * q) * 4;
@@ -753,8 +781,9 @@ struct StreamSrc {
   // the slot of chunk IDX-1.  The operations issued after chunk IDX are the
   // next AHEAD-1 stream chunks and, while IDX < AHEAD, the previous unit's
   // record stores (unless this is the wave's first unit) and the next unit's
-  // q copy.  Without a next unit the wait counts only the chunks that follow
-  // (waiting for more is never wrong).
+  // q copy.  Without a next unit the wait counts only the chunks that follow,
+  // and the next unit's append stores (ahead of its first chunk) are not
+  // counted either (waiting for more is never wrong).
   template <int IDX>
   __device__ __forceinline__ void step() const {
     if (has_next) {
@@ -765,6 +794,9 @@ struct StreamSrc {
         wait_vmcnt_le<LOADS * (AHEAD - 1)>();
       }
       lds_reads_done();
+      // the next unit's first chunk: its append comes first (its staged rows
+      // arrived with its q copy, which the waits so far have covered)
+      if constexpr (APPEND && IDX + AHEAD == 16) append(nxt, nstage);
       issue<IDX + AHEAD>();
     } else {
       wait_vmcnt_le<LOADS * (15 - IDX < AHEAD - 1 ? 15 - IDX : AHEAD - 1)>();
@@ -835,6 +867,20 @@ __device__ __forceinline__ void copy_factors(const float* kf, const float* vf,
   lds_dma16_sv(vf, off, slot + 1024);
 }
 
+// The new key and value rows of a unit's (sequence, kv head) -- the rows of
+// its last position, in [sequence, kv head, D] arrays -- into LDS: the key row
+// at slot, the value row at slot + 1024, 16-byte chunk j at +16j (the lanes
+// past one row's chunks repeat them).  Two direct loads of 1 KiB.
+template <int D>
+__device__ __forceinline__ void copy_new_rows(const uint16_t* k_new, const uint16_t* v_new,
+                                              const DecodeUnit<D>& un, int nkv, uint32_t slot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = ((int64_t)un.b * nkv + un.g) * D;
+  const uint32_t off = (uint32_t)(lane % KV<D>::CPR) * 16u;
+  lds_dma16_sv(k_new + row, off, slot);
+  lds_dma16_sv(v_new + row, off, slot + 1024);
+}
+
 template <int D>
 __device__ __forceinline__ void read_q(const uint8_t* slot, bf16x8 (&qf)[KV<D>::DS]) {
   const int lane = threadIdx.x & (kWave - 1), col = lane & 15, q4 = lane >> 4;
@@ -845,17 +891,23 @@ __device__ __forceinline__ void read_q(const uint8_t* slot, bf16x8 (&qf)[KV<D>::
 
 // Q16: the cache holds int16 codes with per-(page, kv head, slot) factors kf /
 // vf; each unit's 256 key and value factors travel with its q copy into a
-// double-buffered 2 KiB LDS slot of the wave.
+// double-buffered 2 KiB LDS slot of the wave.  Otherwise (bf16 cache) the
+// kernel also appends the call's token: k_new / v_new hold each sequence's
+// new key and value rows ([B, nkv, D]), which belong at position kv_len - 1;
+// the same slots carry them (StreamSrc::append).
 template <int D, int WAVES, int RING, bool Q16>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bi_attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
-    int smax, float c2, const float* __restrict__ kf, const float* __restrict__ vf) {
+    int smax, float c2, const float* __restrict__ kf, const float* __restrict__ vf,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
   using Src = StreamSrc<D, RING, Q16>;
   constexpr int QSLOT = 16 * KV<D>::ROWB;
-  constexpr int FSLOT = Q16 ? 2048 : 0;  // key factors, then value factors
+  // int16 cache: key factors, then value factors; bf16 cache: the new key
+  // row, then the new value row (1 KiB each: one direct load apiece)
+  constexpr int FSLOT = 2048;
   __shared__ __attribute__((aligned(1024)))
   uint8_t lds[WAVES][Src::RING * Src::SLOT + 2 * QSLOT + 2 * FSLOT];
   const int lane = threadIdx.x & (kWave - 1);
@@ -942,6 +994,14 @@ void bi_attn_decode_partial_kernel(
   Src src{kc, vc, ring, &offs, nkv, {}, {}, false, true};
   fill(src.cur, u);
   int qi = 0;
+  if constexpr (Src::APPEND) {
+    // the wave's first unit: its append, when it has one, ahead of everything
+    if (src.cur.last - src.cur.key0 < kSplit) {
+      copy_new_rows<D>(k_new, v_new, src.cur, nkv, fslot0);
+      wait_vmcnt_le<0>();
+      src.append(src.cur, fslot0);
+    }
+  }
   copy_q<D>(q, src.cur.b, src.cur.g, nq, group, qslot0);
   if constexpr (Q16) copy_factors<D>(kf, vf, src.cur, nkv, fslot0);
   src.prologue();
@@ -953,8 +1013,14 @@ void bi_attn_decode_partial_kernel(
     if (src.has_next) {
       fill(src.nxt, un);
       copy_q<D>(q, src.nxt.b, src.nxt.g, nq, group, qslot0 + (uint32_t)(qi ^ 1) * QSLOT);
-      if constexpr (Q16)
+      if constexpr (Q16) {
         copy_factors<D>(kf, vf, src.nxt, nkv, fslot0 + (uint32_t)(qi ^ 1) * FSLOT);
+      } else {
+        // staged for every next unit, so that the wait counts stay fixed;
+        // used only by one that holds its sequence's last position
+        src.nstage = fslot0 + (uint32_t)(qi ^ 1) * FSLOT;
+        copy_new_rows<D>(k_new, v_new, src.nxt, nkv, src.nstage);
+      }
     }
     // Wait for this unit's q copy.  Issued after it: the unit's first AHEAD
     // chunks, the previous unit's record stores (unless this is the wave's
@@ -1029,10 +1095,10 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
   for (int s0 = 1; s0 < ns; s0 += CH) {
     const int n = min(CH, ns - s0);  // splits s0 .. s0+n-1 in this chunk
     // every record value of the thread's dim in the chunk, requested at once
+    // (past the chunk's end the last split stands in: no branch per load)
     float po[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j)
-      if (j < n) po[j] = rec[(int64_t)(s0 + j) * F + t];
+    for (int j = 0; j < CH; ++j) po[j] = rec[(int64_t)(s0 + min(j, n - 1)) * F + t];
     // thread t: split s0+t's max; prefix max over the chunk, carried in
     const float* rt = rec + (int64_t)(s0 + min(t, n - 1)) * F;
     const float ms = t < n ? rt[D] : -INFINITY;
@@ -1059,14 +1125,14 @@ __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restr
     }
     if (t == n - 1) mlast = pm;
     __syncthreads();
-    // the chains, in split order
+    // the chains, in split order; steps past the chunk's end keep the state
+    // by a select, so the chunk is one block
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      if (j < n) {
-        const FoldCoef f{sa[j], sb[j], 0.0f};
-        o = fold_apply(o, po[j], f);
-        l = fold_apply(l, sl[j], f);
-      }
+      const FoldCoef f{sa[j], sb[j], 0.0f};
+      const bool ok = j < n;
+      o = ok ? fold_apply(o, po[j], f) : o;
+      l = ok ? fold_apply(l, sl[j], f) : l;
     }
     M = mlast;
     __syncthreads();  // every read of this chunk's arrays is done
@@ -1463,10 +1529,10 @@ static int decode_workgroups(int64_t units, int waves) {
   return (int)(need < cus ? need : cus);
 }
 
-hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
-                              const int32_t* bt, const void* kc, const void* vc, void* out,
-                              float* lse, int max_splits, float* ws, hipStream_t st,
-                              const float* kf, const float* vf) {
+hipError_t launch_attn_decode(const AttnDims& s, const void* q, const void* k_new,
+                              const void* v_new, const int32_t* kv_len, const int32_t* bt,
+                              void* kc, void* vc, void* out, float* lse, int max_splits, float* ws,
+                              hipStream_t st, const float* kf, const float* vf) {
   const int64_t units = (int64_t)s.B * s.nkv * max_splits;
   const bool q16 = kf != nullptr;
   const int waves = q16 ? kDecodeWaves16 : kDecodeWaves;
@@ -1478,7 +1544,7 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* k
                                                     QQ ? kDecodeSlots16 : kDecodeSlots, QQ>),    \
                      grid1, dim3(64 * waves), 0, st, (const uint16_t*)q, kv_len, bt,             \
                      (const uint16_t*)kc, (const uint16_t*)vc, ws, s.B, s.nq, s.nkv, s.max_pages, \
-                     max_splits, c2, kf, vf)
+                     max_splits, c2, kf, vf, (const uint16_t*)k_new, (const uint16_t*)v_new)
   if (s.d == 128) {
     if (q16)
       BI_DECODE(128, true);

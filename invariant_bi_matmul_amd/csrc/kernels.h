@@ -61,10 +61,15 @@ hipError_t launch_kv_append_i16(const AttnDims& s, const void* k_new, const void
                                 const int32_t* cu_q, const int32_t* kv_len, const int32_t* bt,
                                 void* kc, void* vc, float* kf, float* vf, int max_q_per_seq,
                                 hipStream_t st);
-hipError_t launch_attn_decode(const AttnDims& s, const void* q, const int32_t* kv_len,
-                              const int32_t* bt, const void* kc, const void* vc, void* out,
-                              float* lse, int max_splits, float* ws, hipStream_t st,
-                              const float* kf = nullptr, const float* vf = nullptr);
+// bf16 cache (kf == nullptr): the partial kernel also writes k_new / v_new
+// ([B, nkv, d], one token per sequence) at position kv_len - 1, so no append
+// launch precedes it.  int16 cache: the rows are appended beforehand
+// (launch_kv_append_i16) and k_new / v_new are unused.
+hipError_t launch_attn_decode(const AttnDims& s, const void* q, const void* k_new,
+                              const void* v_new, const int32_t* kv_len, const int32_t* bt,
+                              void* kc, void* vc, void* out, float* lse, int max_splits, float* ws,
+                              hipStream_t st, const float* kf = nullptr,
+                              const float* vf = nullptr);
 hipError_t launch_attn_decode_splitkv(const AttnDims& s, const void* q, const int32_t* kv_len,
                                       const int32_t* bt, const void* kc, const void* vc, void* out,
                                       float* lse, int max_kv_len, int num_splits, float* ws,

@@ -576,10 +576,16 @@ hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int6
   return hipGetLastError();
 }
 
+// The comparator takes bi_matmul's tile for the shape and splits k only to
+// fill CUs that tile leaves idle (the usual split-K heuristic): enough slices
+// for one workgroup per CU, at most 16 and at most one k-tile each.  With one
+// slice it is bi_matmul itself.
 int matmul_splitk_auto(int64_t m, int64_t n, int64_t k) {
-  // Enough slices to give every CU a workgroup, the usual small-M heuristic.
-  const int64_t tiles = ((m + Tile::BM - 1) / Tile::BM) * ((n + Tile::BN - 1) / Tile::BN);
-  int64_t s = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  int bm, bn;
+  int64_t grid;
+  matmul_tile(m, n, &bm, &bn, &grid);
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+  int64_t s = (device_cus() + tiles - 1) / (tiles > 0 ? tiles : 1);
   const int64_t kt = k / Tile::BK;
   if (s > 16) s = 16;
   if (s > kt) s = kt;
@@ -587,15 +593,32 @@ int matmul_splitk_auto(int64_t m, int64_t n, int64_t k) {
   return (int)s;
 }
 
+template <class T>
+static void launch_split(const void* a, const void* w, float* ws, int64_t m, int64_t n, int per,
+                         int used, int64_t k, hipStream_t st) {
+  const int64_t tiles = tile_count<T>(m, n);
+  hipLaunchKernelGGL((bi_matmul_kernel<T, true>), dim3((unsigned)tiles, 1, (unsigned)used),
+                     dim3(T::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
+                     (int)m, (int)n, (int)k, 1, per);
+}
+
 hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,
                                 int64_t n, int64_t k, int split_k, float* ws, hipStream_t st) {
-  const int64_t tiles = ((m + Tile::BM - 1) / Tile::BM) * ((n + Tile::BN - 1) / Tile::BN);
+  if (split_k <= 1) return launch_matmul(a, w, c, c_f32, m, n, k, st);
   const int kt = (int)(k / Tile::BK);
   const int per = (kt + split_k - 1) / split_k;
   const int used = (kt + per - 1) / per;  // slices that own at least one k-tile
-  hipLaunchKernelGGL((bi_matmul_kernel<Tile, true>), dim3((unsigned)tiles, 1, (unsigned)used),
-                     dim3(Tile::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
-                     (int)m, (int)n, (int)k, 1, per);
+  int bm, bn;
+  int64_t grid;
+  matmul_tile(m, n, &bm, &bn, &grid);
+  if (bm == TileS::BM)
+    launch_split<TileS>(a, w, ws, m, n, per, used, k, st);
+  else if (bm == TileN::BM && bn == TileN::BN)
+    launch_split<TileN>(a, w, ws, m, n, per, used, k, st);
+  else if (bm == TileM::BM)
+    launch_split<TileM>(a, w, ws, m, n, per, used, k, st);
+  else
+    launch_split<Tile>(a, w, ws, m, n, per, used, k, st);
   const int64_t count = m * n;
   hipLaunchKernelGGL(bix_matmul_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
                      st, (const float*)ws, c, count, used, c_f32 ? 1 : 0);

@@ -11,10 +11,17 @@ def _extras():
              for m in range(64) for n in (4096, 14336)}
     return {
         "invariance_bitwise": {"matmul": True, "rmsnorm": True, "attn_decode": True},
-        "cost_of_invariance": {"matmul_M%d" % m: {"invariant_ms": 0.1, "splitk_ms": 0.12,
-                                                  "invariant_over_splitk": 0.8333333,
-                                                  "invariant_over_vendor": 1.02}
-                               for m in (1, 16, 64, 256, 2048)},
+        "cost_of_invariance": dict(
+            {"matmul_%s_M%d" % (p, m): {"invariant_ms": 0.1, "splitk_ms": 0.12,
+                                        "invariant_over_splitk": 0.8333333,
+                                        "invariant_over_vendor": 1.02}
+             for m in (1, 16, 64) for p in ("qkv", "o", "gate_up", "down", "lm_head")},
+            matmul_step_2048x4096x14336={"invariant_ms": 0.23, "invariant_over_splitk": 0.8333333,
+                                         "invariant_over_vendor": 1.02},
+            stack_token_ms={m: {"invariant": 3.0, "splitk": 2.5, "vendor": 2.8,
+                                "invariant_over_splitk": 1.2, "invariant_over_vendor": 1.07}
+                            for m in (1, 16, 64)},
+            decode_B64_L4096={"invariant_over_splitkv": 0.87}),
         "sweeps": {"matmul": sweep, "rmsnorm": sweep, "decode": sweep},
         "ceilings": {"read_4GiB": {"GB/s": 6280.123456}},
         "e2e_llama8b": {"config": {"layers": 32},
@@ -63,5 +70,9 @@ def test_line_carries_the_contract_fields():
     assert "extra_field" not in line["components"]["matmul"]
     assert line["failed_extras"] == ["cpu_oracle"]
     assert line["e2e_llama8b"]["invariant"]["unique_outputs_over_30_calls"] == 1
-    assert line["cost_of_invariance"]["matmul_M1"] == {"invariant_over_splitk": 0.8333,
-                                                       "invariant_over_vendor": 1.02}
+    coi = line["cost_of_invariance"]
+    assert coi["matmul_step_2048x4096x14336"] == {"invariant_over_splitk": 0.8333,
+                                                  "invariant_over_vendor": 1.02}
+    assert coi["stack_token_matmuls"]["M1"] == {"invariant_over_splitk": 1.2,
+                                                "invariant_over_vendor": 1.07}
+    assert "matmul_qkv_M1" not in coi and coi["decode_B64_L4096"]["invariant_over_splitkv"] == 0.87
