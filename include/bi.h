@@ -189,7 +189,7 @@ int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, co
  * for that kv head: it writes the rows and then reads them from the pool like
  * every other row, so outputs and pool contents are those of an append
  * followed by attention.  A length beyond max_kv_len leaves its row
- * unwritten and its outputs undefined. */
+ * unwritten and its outputs undefined.
  *   workspace: device, >= bi_attn_workspace_bytes(s, B, max_kv_len) bytes,
  *   contents on entry ignored, scratch for the per-split partials. */
 int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
