@@ -471,16 +471,21 @@ def ceilings():
     out["read_4GiB"] = best
     del src
     fsink = torch.zeros(4, dtype=torch.float32, device="cuda")
-    best = None
     iters = 20000
-    for wg in (CUS * 4, CUS * 8):
-        fl = 4.0 * 4 * 32768 * iters * wg
-        ms = time_call(lambda: bi.bix_mfma_loop(iters, wg, fsink), reps=5, warmup=1)
-        tf = fl / ms / 1e9
-        if best is None or tf > best["TFLOP/s"]:
-            best = {"TFLOP/s": tf, "ms": ms, "workgroups": wg, "waves_per_simd": wg // CUS,
-                    "implied_clock_GHz": tf * 1e12 / (CUS * MFMA_FLOPS_PER_CU_CLK) / 1e9}
-    out["mfma_bf16_loop"] = best
+    # fixed operands, then operands that change from one MFMA to the next (as
+    # in a matmul): the second shows the clock the chip holds under the
+    # matrix pipe's real power draw
+    for key, varied in (("mfma_bf16_loop", False), ("mfma_bf16_loop_varied", True)):
+        best = None
+        for wg in (CUS * 4, CUS * 8):
+            fl = 4.0 * 4 * 32768 * iters * wg
+            ms = time_call(lambda: bi.bix_mfma_loop(iters, wg, fsink, varied=varied), reps=5,
+                           warmup=1)
+            tf = fl / ms / 1e9
+            if best is None or tf > best["TFLOP/s"]:
+                best = {"TFLOP/s": tf, "ms": ms, "workgroups": wg, "waves_per_simd": wg // CUS,
+                        "implied_clock_GHz": tf * 1e12 / (CUS * MFMA_FLOPS_PER_CU_CLK) / 1e9}
+        out[key] = best
     torch.cuda.synchronize()
     return out
 
@@ -938,8 +943,8 @@ def main():
     ap.add_argument("--sweep-parts", default="matmul,rmsnorm,decode,prefill",
                     help="with --only sweeps: which sweeps, comma-separated")
     ap.add_argument("--stage", choices=("rmsnorm", "matmul", "prefill", "decode"),
-                    help="run only this stage of the step, --warmup + --steps times (for "
-                         "profiler passes), and print its average time")
+                    help="run one pass of the step, then only this stage, --warmup + --steps "
+                         "times (for profiler passes), and print its average time")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--extras-out", default=os.path.join("gpurun_out", "bench_extras.json"),
                     help="where the full record (sweeps, ceilings, comparators, e2e, oracle "
@@ -965,6 +970,11 @@ def main():
         print(json.dumps({"sweeps": sweeps(wl, tuple(args.sweep_parts.split(",")))}))
         return
     if args.stage:
+        # one pass of the whole step first, so that the stage's inputs hold
+        # the step's values (the matmul reads the RMSNorm output; MFMA power,
+        # and so the clock, depends on the operand values)
+        for s in wl.STAGES:
+            getattr(wl, s)()
         fn = getattr(wl, args.stage)
         ms = time_call(fn, reps=args.steps, warmup=args.warmup)
         print(json.dumps({"stage": args.stage, "calls": args.steps, "ms": ms}))
@@ -1021,6 +1031,7 @@ def main():
             if "error" not in c:
                 extras["vs_measured_ceilings"] = {
                     "matmul_over_mfma_loop": tflops / c["mfma_bf16_loop"]["TFLOP/s"],
+                    "matmul_over_mfma_loop_varied": tflops / c["mfma_bf16_loop_varied"]["TFLOP/s"],
                     "decode_over_read_stream": comp["attn_decode"]["GB/s"] / c["read_4GiB"]["GB/s"],
                     "rmsnorm_over_copy": comp["rmsnorm"]["GB/s"] / c["copy_4GiB"]["GB/s"]}
             log("bench: size sweeps")

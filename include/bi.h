@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define BI_ABI_VERSION 3
+#define BI_ABI_VERSION 4
 
 typedef enum {
   BI_OK = 0,
@@ -258,9 +258,12 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
 /* bix_mfma_loop: measurement only, the MFMA ceiling.  `workgroups` workgroups
  * of four waves each run `iters` rounds of four independent bf16
  * v_mfma_f32_32x32x16 chains on register operands: 4 * 32768 * iters flops
- * per wave, no memory traffic.  sink: device float, written never (it only
- * keeps the work from being optimised away). */
-int bix_mfma_loop(int64_t iters, int32_t workgroups, float* sink, void* stream);
+ * per wave, no memory traffic.  varied != 0: the chains cycle through four
+ * operand pairs of random-looking bits, so consecutive MFMAs see different
+ * inputs as in a matmul (the pipe's power, and so the clock the chip holds,
+ * depends on the bits); 0: one fixed, smooth pair.  sink: device float,
+ * written never (it only keeps the work from being optimised away). */
+int bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink, void* stream);
 
 /* bix_read_stream: measurement only, the HBM read ceiling.  Reads `bytes`
  * (a multiple of 8192) from device pointer p (16-byte aligned) once, as 8 KiB

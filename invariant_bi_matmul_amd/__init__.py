@@ -108,7 +108,7 @@ def load_library(path: str):
         "bi_swiglu_pair": (ctypes.c_int, [P, P, i64, i64, P]),
         "bi_add": (ctypes.c_int, [P, P, P, i64, P]),
         "bi_argmax": (ctypes.c_int, [P, P, i64, i64, P]),
-        "bix_mfma_loop": (ctypes.c_int, [i64, i32, P, P]),
+        "bix_mfma_loop": (ctypes.c_int, [i64, i32, i32, P, P]),
         "bix_read_stream": (ctypes.c_int, [P, i64, i32, P, P]),
         "bi_attn_prefill_i16": (ctypes.c_int,
                                 [SP, P, P, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
@@ -593,13 +593,15 @@ def attn_decode_i16(q, k_new, v_new, kv_len, block_table, k_cache, v_cache, k_sc
 
 # --------------------------------------------------------------------------- measurement
 
-def bix_mfma_loop(iters: int, workgroups: int, sink: Optional[torch.Tensor] = None):
+def bix_mfma_loop(iters: int, workgroups: int, sink: Optional[torch.Tensor] = None,
+                  varied: bool = False):
     """Measurement only: ``workgroups`` x 4 waves each run ``iters`` rounds of four
-    independent bf16 32x32x16 MFMAs in registers.  Returns the flop count."""
+    independent bf16 32x32x16 MFMAs in registers (``varied``: on operands that
+    change from one MFMA to the next).  Returns the flop count."""
     if sink is None:
         sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    _check("bix_mfma_loop", load().bix_mfma_loop(int(iters), int(workgroups), _ptr(sink),
-                                                 _stream()))
+    _check("bix_mfma_loop", load().bix_mfma_loop(int(iters), int(workgroups), int(bool(varied)),
+                                                 _ptr(sink), _stream()))
     return 4.0 * 4 * 32768 * iters * workgroups
 
 

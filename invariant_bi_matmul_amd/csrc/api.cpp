@@ -492,13 +492,14 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
 
 // ---- measurement ---------------------------------------------------------------
 
-int bix_mfma_loop(int64_t iters, int32_t workgroups, float* sink, void* stream) {
+int bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink, void* stream) {
   try {
     if (iters < 0 || workgroups < 0) return BI_ERR_INVALID_SHAPE;
     if (iters == 0 || workgroups == 0) return BI_OK;
     if (sink == nullptr) return BI_ERR_NULL_POINTER;
     if (!aligned4(sink)) return BI_ERR_INVALID_SHAPE;
-    return hip_status(bi::launch_mfma_loop(iters, workgroups, sink, (hipStream_t)stream));
+    return hip_status(
+        bi::launch_mfma_loop(iters, workgroups, varied != 0, sink, (hipStream_t)stream));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }

@@ -23,7 +23,8 @@ void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid);
 hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
                          int64_t k, hipStream_t st);
 int matmul_splitk_auto(int64_t m, int64_t n, int64_t k);
-hipError_t launch_mfma_loop(int64_t iters, int workgroups, float* sink, hipStream_t st);
+hipError_t launch_mfma_loop(int64_t iters, int workgroups, bool varied, float* sink,
+                            hipStream_t st);
 
 // Debug-build validation of the attention index arrays: bits of *flag.
 constexpr int kCheckLength = 1, kCheckQueries = 2, kCheckPage = 4;

@@ -57,9 +57,9 @@
 namespace bi {
 namespace {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = kMatmulBK>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = kMatmulBK, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_,
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_,
                        STAGES = STAGES_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 32, NI = WN / 32;
@@ -71,8 +71,10 @@ struct TileCfg {
   static constexpr int A_ROW = BK * 2, W_ROW = BN * 2;
   static constexpr int A_CPR = BK / 8, W_CPR = BN / 8;  // 16-byte chunks per row
   static constexpr int GROUP_M = 4;                   // row-tiles per raster group
-  static_assert(BK == 64, "swizzles assume 128-byte A rows");
-  static_assert(BN == 128 || BN == 64, "W swizzles exist for 16 and 8 chunks per k row");
+  static_assert(BK == 64 || BK == 32, "A swizzles exist for 128- and 64-byte rows");
+  static_assert(kMatmulBK % BK == 0, "k-tiles divide the k granularity of the interface");
+  static_assert(BN == 256 || BN == 128 || BN == 64,
+                "W swizzles exist for 32, 16 and 8 chunks per k row");
   static_assert(A_LOADS * NT * 16 == A_BYTES && W_LOADS * NT * 16 == W_BYTES, "tile/threads");
   static_assert(MI * 32 == WM && NI * 32 == WN, "wave tile");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS");
@@ -87,27 +89,39 @@ struct TileCfg {
   // 32-row blocks per wave and A load i filling rows 64i .. 64i+63
   static constexpr bool LIVE_VARIANTS = MI == 2 && A_LOADS == 4 && BM / A_LOADS == 64;
 };
-// The main tile, and three smaller ones for launches whose main-tile grid
-// would leave CUs idle: 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64
-// (four 64 x 32 waves) and 64 x 64 (four 32 x 32 waves).
+// The main tile, a larger one for launches with at least a round of them,
+// and three smaller ones for launches whose main-tile grid would leave CUs
+// idle: 256 x 256 (eight 128 x 64 waves; 32-wide k-tiles, so that four stages
+// fit), 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64 (four 64 x 32
+// waves) and 64 x 64 (four 32 x 32 waves).
 using Tile = TileCfg<256, 128, 4, 2, 3>;
+using TileL = TileCfg<256, 256, 2, 4, 4, 32>;
 using TileM = TileCfg<128, 128, 2, 2, 3>;
 using TileN = TileCfg<128, 64, 2, 2, 4>;
 using TileS = TileCfg<64, 64, 2, 2, 4>;
 
-// A in LDS: [BM rows][8 chunks of 16 B]; chunk c of row r sits at
-// c ^ swz_a(r): the 8 rows an MFMA operand read touches per 128-byte window
-// fall on 8 different 16-byte bank groups.
-__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
+// A in LDS: [BM rows][CPR chunks of 16 B]; chunk c of row r sits at
+// c ^ swz_a(r).  An MFMA operand read takes one chunk position from each of
+// 32 consecutive rows; the 16 lanes the LDS serves together (16 rows, 256 B)
+// then fall on 16 different 16-byte bank groups: for 128-byte rows row pairs
+// already differ by 128 bytes and the XOR spreads the 8 rows of each parity,
+// for 64-byte rows row quads differ by 64 bytes and the XOR spreads the 4
+// rows of each residue mod 4.
+template <int CPR>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
+  else return (r >> 2) & 3;
+}
 // W in LDS: [BK k rows][CPR chunks of 16 B]; chunk c of k row k sits at
 // c ^ swz_w(k), a 64-byte block XOR.  A half-wave's transposing read covers 4
 // consecutive k rows (from a multiple of 4) and 64 bytes of each; the XOR
 // puts those four 64-byte pieces on four different quarters of the 256-byte
-// bank space: by k mod 4 for 256-byte rows (CPR 16), and by bit 1 of k for
-// 128-byte rows (CPR 8), whose row pairs already differ by 128 bytes.
+// bank space: by k mod 4 for rows of 256 or 512 bytes (CPR 16, 32), and by
+// bit 1 of k for 128-byte rows (CPR 8), whose row pairs already differ by 128
+// bytes.
 template <int CPR>
 __device__ __forceinline__ int swz_w(int k) {
-  if constexpr (CPR == 16) return (k & 3) << 2;
+  if constexpr (CPR >= 16) return (k & 3) << 2;
   else return ((k >> 1) & 1) << 2;
 }
 
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < T::A_LOADS; ++i) {
       const int q = i * NT + wave * 64 + lane;
-      const int row = q / T::A_CPR, c = (q % T::A_CPR) ^ swz_a(q / T::A_CPR);
+      const int row = q / T::A_CPR, c = (q % T::A_CPR) ^ swz_a<T::A_CPR>(q / T::A_CPR);
       a_off[i] = (uint32_t)(((int64_t)(min(m0 + row, M - 1) - m0) * K + c * 8) * 2);
     }
 #pragma unroll
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
     for (int mi = 0; mi < MI; ++mi) {
       const int r = wave_m * T::WM + mi * 32 + (lane & 31);
       const int ch = 2 * kk + (lane >> 5);
-      ao[kk][mi] = (uint32_t)(r * T::A_ROW + ((ch ^ swz_a(r)) << 4));
+      ao[kk][mi] = (uint32_t)(r * T::A_ROW + ((ch ^ swz_a<T::A_CPR>(r)) << 4));
     }
   // B operand, block ni: lane l needs W[16kk + 8(l/32) + e][col + l%32],
   // e = 0..7, as two transposed reads of 4 k rows; within a 16-lane group,
@@ -529,14 +543,15 @@ static int64_t tile_count(int64_t m, int64_t n) {
 }
 
 // The tile: the first of 64 x 64, 128 x 64 and 128 x 128 whose tiles number at
-// most one per CU, else the main tile (persistent, at most one workgroup per
-// CU).  A smaller
-// tile moves more bytes per flop from L2 to LDS, and the smaller tiles run one
-// wave per SIMD; so past one round of tiles the main tile's fewer, denser
-// tiles finish first.  All four run the same MFMA instruction on the same
-// operands in the same k order for every output element (a row or column's
-// place inside a 32 x 32 block is its index mod 32 under each tile), so the
-// choice changes no bits.
+// most one per CU; else, with several row-tiles, 256 x 256 where its rounds of
+// tiles are estimated to finish first, else the main tile (both persistent,
+// at most one workgroup per CU).  A smaller tile moves more bytes per flop
+// from L2 to LDS, and the smaller tiles run one wave per SIMD; so past one
+// round of tiles the larger tiles' fewer, denser tiles finish first.  All
+// five run the same MFMA instruction on the same operands in the same k order
+// for every output element (a row or column's place inside a 32 x 32 block is
+// its index mod 32 under each tile, and the k-tile width only groups the same
+// ascending 16-wide steps), so the choice changes no bits.
 template <class T>
 static void launch_tile(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
                         int64_t k, int64_t grid, hipStream_t st) {
@@ -556,7 +571,15 @@ void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid) {
   } else if (tm <= cus) {
     *bm = TileM::BM, *bn = TileM::BN, *grid = tm;
   } else {
-    *bm = Tile::BM, *bn = Tile::BN, *grid = std::min(tile_count<Tile>(m, n), cus);
+    // persistent: each CU runs ceil(tiles / CUs) tiles back to back, and a
+    // 256 x 256 tile takes about 1.6 times a 256 x 128 one (measured at
+    // 2048 x 4096 x 14336: 93 against 59 us per tile)
+    const int64_t tl = tile_count<TileL>(m, n), tt = tile_count<Tile>(m, n);
+    if (m > TileL::BM && 8 * ((tl + cus - 1) / cus) < 5 * ((tt + cus - 1) / cus)) {
+      *bm = TileL::BM, *bn = TileL::BN, *grid = std::min(tl, cus);
+    } else {
+      *bm = Tile::BM, *bn = Tile::BN, *grid = std::min(tt, cus);
+    }
   }
 }
 
@@ -571,6 +594,8 @@ hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int6
     launch_tile<TileN>(a, w, c, c_f32, m, n, k, grid, st);
   else if (bm == TileM::BM)
     launch_tile<TileM>(a, w, c, c_f32, m, n, k, grid, st);
+  else if (bn == TileL::BN)
+    launch_tile<TileL>(a, w, c, c_f32, m, n, k, grid, st);
   else
     launch_tile<Tile>(a, w, c, c_f32, m, n, k, grid, st);
   return hipGetLastError();
@@ -593,32 +618,36 @@ int matmul_splitk_auto(int64_t m, int64_t n, int64_t k) {
   return (int)s;
 }
 
+// k cut into split_k slices of whole k-tiles of the tile's width; returns the
+// slices that own at least one k-tile (at most split_k).
 template <class T>
-static void launch_split(const void* a, const void* w, float* ws, int64_t m, int64_t n, int per,
-                         int used, int64_t k, hipStream_t st) {
+static int launch_split(const void* a, const void* w, float* ws, int64_t m, int64_t n,
+                        int split_k, int64_t k, hipStream_t st) {
+  const int kt = (int)(k / T::BK);
+  const int per = (kt + split_k - 1) / split_k;
+  const int used = (kt + per - 1) / per;
   const int64_t tiles = tile_count<T>(m, n);
   hipLaunchKernelGGL((bi_matmul_kernel<T, true>), dim3((unsigned)tiles, 1, (unsigned)used),
                      dim3(T::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
                      (int)m, (int)n, (int)k, 1, per);
+  return used;
 }
 
 hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,
                                 int64_t n, int64_t k, int split_k, float* ws, hipStream_t st) {
   if (split_k <= 1) return launch_matmul(a, w, c, c_f32, m, n, k, st);
-  const int kt = (int)(k / Tile::BK);
-  const int per = (kt + split_k - 1) / split_k;
-  const int used = (kt + per - 1) / per;  // slices that own at least one k-tile
   int bm, bn;
   int64_t grid;
   matmul_tile(m, n, &bm, &bn, &grid);
+  int used;
   if (bm == TileS::BM)
-    launch_split<TileS>(a, w, ws, m, n, per, used, k, st);
+    used = launch_split<TileS>(a, w, ws, m, n, split_k, k, st);
   else if (bm == TileN::BM && bn == TileN::BN)
-    launch_split<TileN>(a, w, ws, m, n, per, used, k, st);
+    used = launch_split<TileN>(a, w, ws, m, n, split_k, k, st);
   else if (bm == TileM::BM)
-    launch_split<TileM>(a, w, ws, m, n, per, used, k, st);
-  else
-    launch_split<Tile>(a, w, ws, m, n, per, used, k, st);
+    used = launch_split<TileM>(a, w, ws, m, n, split_k, k, st);
+  else  // 256 x 256 (whose one-slice launch has no registers to spare) or the main tile
+    used = launch_split<Tile>(a, w, ws, m, n, split_k, k, st);
   const int64_t count = m * n;
   hipLaunchKernelGGL(bix_matmul_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
                      st, (const float*)ws, c, count, used, c_f32 ? 1 : 0);

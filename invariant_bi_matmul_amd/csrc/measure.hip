@@ -5,7 +5,12 @@
 // v_mfma_f32_32x32x16_bf16 chains on register operands, with no memory
 // traffic, so the only limit is the matrix pipe and its clock.  Four chains
 // of one 32-cycle MFMA each keep a chain's next MFMA 128 cycles behind its
-// previous one, past the instruction's latency.
+// previous one, past the instruction's latency.  The pipe's power, and so the
+// clock the chip can hold, depends on the operand bits: with VARIED the four
+// chains cycle through four operand pairs of hashed bits (random sign and
+// mantissa, magnitude in [1/16, 1)), so that each MFMA's inputs differ from
+// the previous one's as they do in a matmul; otherwise every MFMA takes the
+// same smooth, slowly varying pair.
 //
 // bix_read_stream_kernel gives the HBM read ceiling the way the decode kernel
 // reads: each wave pulls 8 KiB chunks (chunks w, w + NW, ... of the buffer)
@@ -17,18 +22,48 @@
 namespace bi {
 namespace {
 
+__device__ __forceinline__ uint32_t mix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x7feb352du;
+  h ^= h >> 15;
+  h *= 0x846ca68bu;
+  h ^= h >> 16;
+  return h;
+}
+
+template <bool VARIED>
 __global__ __launch_bounds__(256) void bix_mfma_loop_kernel(int64_t iters, float* sink) {
   const int lane = threadIdx.x & 63;
-  bf16x8 a, b;
+  bf16x8 a[4], b[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    a[j] = (__bf16)(0.001f * (float)(lane + j));
-    b[j] = (__bf16)(0.002f * (float)(lane - j));
-  }
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (VARIED) {
+        const uint32_t h = mix32((uint32_t)(lane * 64 + j * 4 + p) * 2654435761u + 1u);
+        // sign, exponent 123..126, 7 mantissa bits
+        const uint16_t ab = (uint16_t)(((h & 1u) << 15) | ((123u + ((h >> 1) & 3u)) << 7) |
+                                       ((h >> 3) & 0x7fu));
+        const uint16_t bb = (uint16_t)((((h >> 10) & 1u) << 15) |
+                                       ((123u + ((h >> 11) & 3u)) << 7) | ((h >> 13) & 0x7fu));
+        a[p][j] = __builtin_bit_cast(__bf16, ab);
+        b[p][j] = __builtin_bit_cast(__bf16, bb);
+      } else {
+        a[p][j] = (__bf16)(0.001f * (float)(lane + j));
+        b[p][j] = (__bf16)(0.002f * (float)(lane - j));
+      }
+    }
   f32x16 acc[4] = {};
-  for (int64_t i = 0; i < iters; ++i) {
+  int64_t i = 0;
+  for (; i + 4 <= iters; i += 4) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = mfma32(a, b, acc[c]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] = mfma32(a[(u + c) & 3], b[(u + c) & 3], acc[c]);
+  }
+  for (; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = mfma32(a[c], b[c], acc[c]);
   }
   // Fold the accumulators and store only on a value they never take, so the
   // loop is kept but nothing is written.
@@ -83,9 +118,14 @@ hipError_t launch_read_stream(const void* p, int64_t bytes, int workgroups, uint
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_loop(int64_t iters, int workgroups, float* sink, hipStream_t st) {
-  hipLaunchKernelGGL(bix_mfma_loop_kernel, dim3((unsigned)workgroups), dim3(256), 0, st, iters,
-                     sink);
+hipError_t launch_mfma_loop(int64_t iters, int workgroups, bool varied, float* sink,
+                            hipStream_t st) {
+  if (varied)
+    hipLaunchKernelGGL(bix_mfma_loop_kernel<true>, dim3((unsigned)workgroups), dim3(256), 0, st,
+                       iters, sink);
+  else
+    hipLaunchKernelGGL(bix_mfma_loop_kernel<false>, dim3((unsigned)workgroups), dim3(256), 0, st,
+                       iters, sink);
   return hipGetLastError();
 }
 

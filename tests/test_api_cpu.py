@@ -43,11 +43,11 @@ def test_debug_build_exports_the_same_functions():
     dbg = ctypes.CDLL(_build.DEBUG_LIB)
     for n in declared_functions():
         assert hasattr(dbg, n), n
-    assert dbg.bi_abi_version() == 3
+    assert dbg.bi_abi_version() == 4
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bi_abi_version() == 3
+    assert lib.bi_abi_version() == 4
     for s in range(7):
         assert lib.bi_status_string(s)
     assert lib.bi_status_string(99) == b"unknown status"
@@ -85,13 +85,19 @@ def test_matmul_validation(lib):
 def test_matmul_tile_choice(lib):
     """The tile bi_matmul picks (256 CUs, the MI355X count and the host-only
     fallback): the first of 64 x 64, 128 x 64, 128 x 128 whose tiles fit one
-    per CU, else the persistent 256 x 128 tile."""
+    per CU; else, with several row-tiles, the persistent 256 x 256 tile where
+    ceil(tiles / CUs) rounds at 1.6 times the time per tile beat those of the
+    persistent 256 x 128 tile, else the latter."""
     import invariant_bi_matmul_amd as bi
     cases = {(1, 4096): (64, 64, 64), (256, 4096): (64, 64, 256), (257, 4096): (128, 64, 192),
              (512, 4096): (128, 64, 256), (513, 4096): (128, 128, 160),
              (1024, 4096): (128, 128, 256), (1025, 4096): (256, 128, 160),
-             (2048, 14336): (256, 128, 256), (64, 28672): (128, 128, 224),
-             (1, 128256): (256, 128, 256), (5, 8): (64, 64, 1)}
+             (2048, 4096): (256, 128, 256), (4096, 4096): (256, 256, 256),
+             (1536, 14336): (256, 128, 256), (1537, 14336): (256, 256, 256),
+             (2048, 14336): (256, 256, 256), (2048, 6144): (256, 256, 192),
+             (64, 28672): (128, 128, 224), (1, 128256): (256, 128, 256),
+             (256, 128256): (256, 128, 256), (300, 128256): (256, 256, 256),
+             (5, 8): (64, 64, 1)}
     for (m, n), want in cases.items():
         assert bi.matmul_tile(m, n) == want, (m, n)
     assert lib.bix_matmul_tile(0, 4096, None, None, None) == SHAPE

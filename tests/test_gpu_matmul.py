@@ -51,9 +51,10 @@ def test_row_invariance_across_m(n):
     # the workload's M, M on both sides of the single-row-tile variants (A
     # loads for rows 0..63, 0..127, all 256), and M that select each tile
     # (N = 4096: 64 x 64 up to 256, 128 x 64 to 512, 128 x 128 to 1024, then
-    # the main tile)
+    # the main tile; N = 14336: 64 x 64 to 64, 128 x 128 to 256, the main
+    # tile to 1536, then 256 x 256)
     for m in list(M_SET[:-1]) + [33, 65, 100, 128, 129, 200, 255, 257, 513, 768, 1024, 1025,
-                                 1536]:
+                                 1536, 1537]:
         c = _mm(a[:m], None, w_dev=wd)
         assert np.array_equal(c, full[:m]), m
     # a row at many different positions inside tiles and batches
@@ -97,10 +98,14 @@ def test_one_hot_rows_select_w():
 @pytest.mark.parametrize("m,n,k", [(5, 8, 64), (33, 264, 128), (257, 520, 192), (1, 4104, 256),
                                    (100, 264, 320), (64, 136, 64),
                                    # ragged in both M and N under each larger tile
-                                   (500, 2056, 192), (1000, 2056, 128), (2100, 4104, 128)])
+                                   (500, 2056, 192), (1000, 2056, 128), (1100, 4104, 128),
+                                   (2100, 4104, 128),
+                                   # fewer k-tiles than the 256 x 256 tile's ring holds
+                                   (2100, 4104, 64)])
 def test_ragged_shapes(orc, m, n, k):
     import invariant_bi_matmul_amd as bi
-    tile = {(500, 2056): (128, 64), (1000, 2056): (128, 128), (2100, 4104): (256, 128)}
+    tile = {(500, 2056): (128, 64), (1000, 2056): (128, 128), (1100, 4104): (256, 128),
+            (2100, 4104): (256, 256)}
     if (m, n) in tile:
         assert bi.matmul_tile(m, n)[:2] == tile[(m, n)]
     a, w = synth.matmul_inputs(m, n, k, seed=5)

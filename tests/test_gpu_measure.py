@@ -31,5 +31,6 @@ def test_mfma_loop_runs_and_writes_nothing():
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
     assert bi.bix_mfma_loop(100, 512, sink) == 4.0 * 4 * 32768 * 100 * 512
     assert bi.bix_mfma_loop(0, 512, sink) == 0.0
+    assert bi.bix_mfma_loop(101, 512, sink, varied=True) == 4.0 * 4 * 32768 * 101 * 512
     torch.cuda.synchronize()
     assert sink.tolist() == [0.0, 0.0, 0.0, 0.0]
