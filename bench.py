@@ -219,9 +219,21 @@ STACK_MATMULS = {"qkv": (4096, 6144), "o": (4096, 4096), "gate_up": (4096, 28672
                  "down": (14336, 4096), "lm_head": (4096, 128256)}
 
 
+def time_alternating(fns, rounds=2, reps=20, warmup=3):
+    """Each call timed `rounds` times with the calls taking turns, and the best
+    of each kept, so that neither side of a ratio is the one timed while the
+    clock or the caches were still settling."""
+    best = [None] * len(fns)
+    for _ in range(rounds):
+        for i, f in enumerate(fns):
+            t = time_call(f, reps=reps, warmup=warmup)
+            best[i] = t if best[i] is None else min(best[i], t)
+    return best
+
+
 def comparators(wl):
     """Invariant kernel vs its non-invariant comparator on the same inputs (ms),
-    warm.  Matmul: the decoder stack's projection shapes at M = 1, 16, 64 (the
+    warm, timed in turns (best of two).  Matmul: the decoder stack's projection shapes at M = 1, 16, 64 (the
     decode batches) and the step's 2048 x 4096 x 14336, each beside split-K
     (bi_matmul's tile with k split to fill idle CUs) and the vendor GEMM
     (torch.matmul, not batch-invariant); `stack_token_ms` adds up one decode
@@ -248,9 +260,10 @@ def comparators(wl):
         a = a_big[:m, :k].contiguous()
         c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
         need = lib.bix_matmul_workspace_bytes(m, n, k, 0)
-        ti = time_call(lambda: bi.matmul(a, w, out=c))
-        tc = time_call(lambda: bi.bix_matmul_splitk(a, w, out=c, workspace=ws[:need // 4 + 4]))
-        tv = time_call(lambda: torch.matmul(a, w, out=c))
+        ti, tc, tv = time_alternating([
+            lambda: bi.matmul(a, w, out=c),
+            lambda: bi.bix_matmul_splitk(a, w, out=c, workspace=ws[:need // 4 + 4]),
+            lambda: torch.matmul(a, w, out=c)])
         splits = max(1, need // (4 * m * n))
         out["matmul_" + label] = {"invariant_ms": ti, "splitk_ms": tc, "vendor_ms": tv,
                                   "splitk_slices": splits,
@@ -269,8 +282,9 @@ def comparators(wl):
         xr = wl.x[:r].contiguous()
         wsr = torch.empty(r * 64, dtype=torch.float32, device=dev)
         yr = torch.empty_like(xr)
-        ti = time_call(lambda: bi.rmsnorm(xr, wl.g, wl.eps, out=yr))
-        tc = time_call(lambda: bi.bix_rmsnorm_splitrow(xr, wl.g, wl.eps, out=yr, workspace=wsr))
+        ti, tc = time_alternating([
+            lambda: bi.rmsnorm(xr, wl.g, wl.eps, out=yr),
+            lambda: bi.bix_rmsnorm_splitrow(xr, wl.g, wl.eps, out=yr, workspace=wsr)])
         out["rmsnorm_rows%d" % r] = {"invariant_ms": ti, "splitrow_ms": tc,
                                      "invariant_over_splitrow": ti / tc}
     for bsz in (1, 8, 64):
@@ -279,8 +293,8 @@ def comparators(wl):
                 wl.kvl_dec[sl].contiguous(), wl.bt_dec[sl].contiguous(), wl.kc, wl.vc, wl.scale,
                 L_MAX)
         o = torch.empty(bsz, NQ, D, dtype=torch.bfloat16, device=dev)
-        ti = time_call(lambda: bi.attn_decode(*args, out=o))
-        tc = time_call(lambda: bi.bix_attn_decode_splitkv(*args, out=o))
+        ti, tc = time_alternating([lambda: bi.attn_decode(*args, out=o),
+                                   lambda: bi.bix_attn_decode_splitkv(*args, out=o)])
         out["decode_B%d_L%d" % (bsz, L_MAX)] = {"invariant_ms": ti, "splitkv_ms": tc,
                                                 "invariant_over_splitkv": ti / tc}
     torch.cuda.synchronize()

@@ -14,10 +14,14 @@
 //     workspace and a second kernel folds them; both run the same functions on
 //     the same operand values, so a token's output row has the same bits
 //     either way.  Operands always come from LDS with the same layout; only
-//     how they get there differs: decode streams each wave's split through a
-//     wave-private ring of 5 chunk slots (RingSrc), prefill copies a whole
-//     split into LDS for the waves of a workgroup to share (StagedSrc).
-//     Both copy with direct global->LDS loads whose page is wave-uniform.
+//     how they get there differs: decode streams each wave's units through a
+//     wave-private ring of 8 chunk slots (StreamSrc; 4 for the int16 cache),
+//     prefill copies a whole split into LDS for the waves of a workgroup to
+//     share (StagedSrc), and the split-count comparator streams each split
+//     through a ring of 5 slots (RingSrc).  All copy with direct global->LDS
+//     loads whose page is wave-uniform.  (bf16 decode appends inside its split
+//     pass: the one wave that reads a sequence's last split for a kv head
+//     stores the new rows before it loads them.)
 //
 // Work unit: one wave64 computes the partial of one split for NB blocks of 16
 // query columns (GQA: the columns of a block are (position, head-of-group)
@@ -27,10 +31,12 @@
 // Keys of a 32-key chunk are permuted onto MFMA rows so that each lane's
 // accumulator holds the 8 consecutive keys it needs as the P^T operand; the
 // V^T operand is read from LDS with the transposing load ds_read_b64_tr_b16.
-// All 8 chunks of a split are always computed.  Keys beyond a column's
-// position get logit -inf and weight exactly 0, and their addresses are
-// clamped to the last written position, so they add exact zeros: a split's
-// bits do not depend on how far past the query the split's keys run.
+// All 8 chunks of a split that starts at or before a column's position are
+// computed (a split wholly past every column of a wave is never visited).
+// Keys beyond a column's position get logit -inf and weight exactly 0, and
+// their addresses are clamped to the last written position, so they add exact
+// zeros: a split's bits do not depend on how far past the query the split's
+// keys run.
 //
 // bix_attn_decode_splitkv_* is the comparator from the problem column of the
 // same row: the key range of each sequence is cut into a number of splits
@@ -1450,20 +1456,6 @@ hipError_t launch_kv_append(const AttnDims& s, const void* k_new, const void* v_
 
 // The wide prefill workgroup: NB blocks per wave x WAVES waves (NB * WAVES = 8).
 constexpr int kWideNB = 1, kWideWaves = 8;
-
-// Compute units of the current device (256 on MI355X), asked once.
-static int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 hipError_t launch_attn_prefill(const AttnDims& s, const void* q, const int32_t* cu_q,
                                const int32_t* kv_len, const int32_t* bt, const void* kc,

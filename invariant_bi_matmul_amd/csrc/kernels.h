@@ -16,6 +16,9 @@ hipError_t launch_rmsnorm_splitrow(const void* x, const void* gamma, void* y, fl
                                    hipStream_t st);
 int rmsnorm_splitrow_auto_chunks(int64_t rows);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 // ---- matmul ----------------------------------------------------------------
 constexpr int kMatmulBK = 64;
 // The tile launch_matmul uses for an m x n product (bm x bn) and its grid.

@@ -49,6 +49,7 @@
 // same row: split-K with a split count chosen from the grid size (so from M),
 // fp32 partials summed by a second kernel.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -523,18 +524,22 @@ __global__ __launch_bounds__(256) void bix_matmul_reduce_kernel(const float* __r
 
 }  // namespace
 
-// Compute units of the current device (one persistent workgroup each).
-static int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+// Compute units of the current device (one persistent workgroup each), asked
+// once per device and kept for the process (256, the MI355X count, if the
+// runtime cannot say).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cus;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <class T>
