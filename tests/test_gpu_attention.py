@@ -138,6 +138,35 @@ def test_decode_batch_companions_and_position():
         assert np.array_equal(r, results[0])
 
 
+def test_decode_append_writes_exactly_the_new_rows():
+    """The decode call appends its token inside the split pass.  After one
+    decode step every pool row is what it was, except each sequence's new
+    position, which holds that token's key and value rows bitwise: new
+    positions 0, 255 (the last key of a full split), 256 (a split's first
+    key), mid-split, 511 and 4095.  Unused pages stay NaN-poisoned."""
+    from helpers import bits_of
+    lens = [1, 256, 257, 300, 512, 4096]
+    prob = _gqa(lens, seed=11)
+    run = PagedRun(prob, page_seed=4)
+    run.prefill([(b, L - 1) for b, L in enumerate(lens) if L > 1])
+    k_before, v_before = bits_of(run.kc), bits_of(run.vc)
+    run.decode(list(range(len(lens))))
+    want_k, want_v = k_before.copy(), v_before.copy()
+    for b, L in enumerate(lens):
+        pos = L - 1
+        page = run.bt_host[b, pos // 16]
+        want_k[page, :, pos % 16, :] = prob.k[b][pos]
+        want_v[page, :, pos % 16, :] = prob.v[b][pos]
+    assert np.array_equal(bits_of(run.kc), want_k)
+    assert np.array_equal(bits_of(run.vc), want_v)
+    # and the rows the step attended over include the new one: its output
+    # equals a one-shot prefill of the whole sequence
+    one = PagedRun(prob, page_seed=5)
+    one.prefill([(b, L) for b, L in enumerate(lens)])
+    for b, L in enumerate(lens):
+        assert np.array_equal(run.out[b][L - 1], one.out[b][L - 1]), b
+
+
 def test_long_context_32768(orc):
     L = 32768
     prob = _gqa([L], seed=9)
