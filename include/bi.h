@@ -106,10 +106,11 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t r
  * w  bf16 [k, n] row-major (n contiguous).
  * c  [m, n] row-major, bf16 (rounded from the fp32 sum) or fp32 per c_dtype.
  * One bf16 MFMA instruction for every m, n, k; each element's k-loop runs in
- * one fixed order (64-wide k-tiles, 16-wide MFMA steps, ascending); no
- * split-K.  The output tile (256 x 128; 128 x 128, 128 x 64 or 64 x 64 for launches
- * too small to give the main tile every CU; bix_matmul_tile reports it) only
- * decides which wave computes an element, never its bits.  The bf16 result
+ * one fixed order (16-wide MFMA steps, ascending); no split-K.  The output
+ * tile (256 x 256 or 256 x 128 for launches with a round of them; 128 x 128,
+ * 128 x 64, 64 x 64 or 64 x 32 for launches too small to give those every CU;
+ * bix_matmul_tile reports it) only decides which wave computes an element,
+ * never its bits.  The bf16 result
  * is exactly the round-to-nearest-even of the fp32 result.
  * Requires k % 64 == 0, n % 8 == 0, k <= 2^22 and n <= 2^24 (else
  * BI_ERR_UNSUPPORTED).

@@ -74,8 +74,8 @@ struct TileCfg {
   static constexpr int GROUP_M = 4;                   // row-tiles per raster group
   static_assert(BK == 64 || BK == 32, "A swizzles exist for 128- and 64-byte rows");
   static_assert(kMatmulBK % BK == 0, "k-tiles divide the k granularity of the interface");
-  static_assert(BN == 256 || BN == 128 || BN == 64,
-                "W swizzles exist for 32, 16 and 8 chunks per k row");
+  static_assert(BN == 256 || BN == 128 || BN == 64 || BN == 32,
+                "W swizzles exist for 32, 16, 8 and 4 chunks per k row");
   static_assert(A_LOADS * NT * 16 == A_BYTES && W_LOADS * NT * 16 == W_BYTES, "tile/threads");
   static_assert(MI * 32 == WM && NI * 32 == WN, "wave tile");
   static_assert(STAGES * STAGE <= 160 * 1024, "LDS");
@@ -91,15 +91,17 @@ struct TileCfg {
   static constexpr bool LIVE_VARIANTS = MI == 2 && A_LOADS == 4 && BM / A_LOADS == 64;
 };
 // The main tile, a larger one for launches with at least a round of them,
-// and three smaller ones for launches whose main-tile grid would leave CUs
+// and four smaller ones for launches whose main-tile grid would leave CUs
 // idle: 256 x 256 (eight 128 x 64 waves; 32-wide k-tiles, so that four stages
 // fit), 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64 (four 64 x 32
-// waves) and 64 x 64 (four 32 x 32 waves).
+// waves), 64 x 64 (four 32 x 32 waves) and 64 x 32 (two 32 x 32 waves, twice
+// the workgroups on W of a small-M launch).
 using Tile = TileCfg<256, 128, 4, 2, 3>;
 using TileL = TileCfg<256, 256, 2, 4, 4, 32>;
 using TileM = TileCfg<128, 128, 2, 2, 3>;
 using TileN = TileCfg<128, 64, 2, 2, 4>;
 using TileS = TileCfg<64, 64, 2, 2, 4>;
+using TileT = TileCfg<64, 32, 2, 1, 6>;
 
 // A in LDS: [BM rows][CPR chunks of 16 B]; chunk c of row r sits at
 // c ^ swz_a(r).  An MFMA operand read takes one chunk position from each of
@@ -123,7 +125,8 @@ __device__ __forceinline__ int swz_a(int r) {
 template <int CPR>
 __device__ __forceinline__ int swz_w(int k) {
   if constexpr (CPR >= 16) return (k & 3) << 2;
-  else return ((k >> 1) & 1) << 2;
+  else if constexpr (CPR == 8) return ((k >> 1) & 1) << 2;
+  else return 0;  // 64-byte rows: the four k rows are 256 contiguous bytes
 }
 
 // Position of raster id `id` (groups of GROUP_M row-tiles; row-tiles fastest
@@ -547,13 +550,13 @@ static int64_t tile_count(int64_t m, int64_t n) {
   return ((m + T::BM - 1) / T::BM) * ((n + T::BN - 1) / T::BN);
 }
 
-// The tile: the first of 64 x 64, 128 x 64 and 128 x 128 whose tiles number at
-// most one per CU; else, with several row-tiles, 256 x 256 where its rounds of
-// tiles are estimated to finish first, else the main tile (both persistent,
-// at most one workgroup per CU).  A smaller tile moves more bytes per flop
-// from L2 to LDS, and the smaller tiles run one wave per SIMD; so past one
-// round of tiles the larger tiles' fewer, denser tiles finish first.  All
-// five run the same MFMA instruction on the same operands in the same k order
+// The tile: the first of 64 x 32, 64 x 64, 128 x 64 and 128 x 128 whose tiles
+// number at most one per CU; else, with several row-tiles, 256 x 256 where its
+// rounds of tiles are estimated to finish first, else the main tile (both
+// persistent, at most one workgroup per CU).  A smaller tile moves more bytes
+// per flop from L2 to LDS, and the smaller tiles run one wave per SIMD; so
+// past one round of tiles the larger tiles' fewer, denser tiles finish first.
+// All six run the same MFMA instruction on the same operands in the same k order
 // for every output element (a row or column's place inside a 32 x 32 block is
 // its index mod 32 under each tile, and the k-tile width only groups the same
 // ascending 16-wide steps), so the choice changes no bits.
@@ -568,8 +571,10 @@ static void launch_tile(const void* a, const void* w, void* c, bool c_f32, int64
 void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid) {
   const int64_t cus = device_cus();
   const int64_t ts = tile_count<TileS>(m, n), tn = tile_count<TileN>(m, n);
-  const int64_t tm = tile_count<TileM>(m, n);
-  if (ts <= cus) {
+  const int64_t tm = tile_count<TileM>(m, n), tq = tile_count<TileT>(m, n);
+  if (tq <= cus) {
+    *bm = TileT::BM, *bn = TileT::BN, *grid = tq;
+  } else if (ts <= cus) {
     *bm = TileS::BM, *bn = TileS::BN, *grid = ts;
   } else if (tn <= cus) {
     *bm = TileN::BM, *bn = TileN::BN, *grid = tn;
@@ -593,7 +598,9 @@ hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int6
   int bm, bn;
   int64_t grid;
   matmul_tile(m, n, &bm, &bn, &grid);
-  if (bm == TileS::BM)
+  if (bm == TileT::BM && bn == TileT::BN)
+    launch_tile<TileT>(a, w, c, c_f32, m, n, k, grid, st);
+  else if (bm == TileS::BM)
     launch_tile<TileS>(a, w, c, c_f32, m, n, k, grid, st);
   else if (bm == TileN::BM && bn == TileN::BN)
     launch_tile<TileN>(a, w, c, c_f32, m, n, k, grid, st);
@@ -645,7 +652,9 @@ hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f3
   int64_t grid;
   matmul_tile(m, n, &bm, &bn, &grid);
   int used;
-  if (bm == TileS::BM)
+  if (bm == TileT::BM && bn == TileT::BN)
+    used = launch_split<TileT>(a, w, ws, m, n, split_k, k, st);
+  else if (bm == TileS::BM)
     used = launch_split<TileS>(a, w, ws, m, n, split_k, k, st);
   else if (bm == TileN::BM && bn == TileN::BN)
     used = launch_split<TileN>(a, w, ws, m, n, split_k, k, st);

@@ -84,12 +84,14 @@ def test_matmul_validation(lib):
 
 def test_matmul_tile_choice(lib):
     """The tile bi_matmul picks (256 CUs, the MI355X count and the host-only
-    fallback): the first of 64 x 64, 128 x 64, 128 x 128 whose tiles fit one
+    fallback): the first of 64 x 32, 64 x 64, 128 x 64, 128 x 128 whose tiles fit one
     per CU; else, with several row-tiles, the persistent 256 x 256 tile where
     ceil(tiles / CUs) rounds at 1.6 times the time per tile beat those of the
     persistent 256 x 128 tile, else the latter."""
     import invariant_bi_matmul_amd as bi
-    cases = {(1, 4096): (64, 64, 64), (256, 4096): (64, 64, 256), (257, 4096): (128, 64, 192),
+    cases = {(1, 4096): (64, 32, 128), (128, 4096): (64, 32, 256), (129, 4096): (64, 64, 192),
+             (1, 6144): (64, 32, 192), (1, 14336): (64, 64, 224),
+             (256, 4096): (64, 64, 256), (257, 4096): (128, 64, 192),
              (512, 4096): (128, 64, 256), (513, 4096): (128, 128, 160),
              (1024, 4096): (128, 128, 256), (1025, 4096): (256, 128, 160),
              (2048, 4096): (256, 128, 256), (4096, 4096): (256, 256, 256),
@@ -97,7 +99,7 @@ def test_matmul_tile_choice(lib):
              (2048, 14336): (256, 256, 256), (2048, 6144): (256, 256, 192),
              (64, 28672): (128, 128, 224), (1, 128256): (256, 128, 256),
              (256, 128256): (256, 128, 256), (300, 128256): (256, 256, 256),
-             (5, 8): (64, 64, 1)}
+             (5, 8): (64, 32, 1)}
     for (m, n), want in cases.items():
         assert bi.matmul_tile(m, n) == want, (m, n)
     assert lib.bix_matmul_tile(0, 4096, None, None, None) == SHAPE

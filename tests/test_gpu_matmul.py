@@ -50,9 +50,9 @@ def test_row_invariance_across_m(n):
     full = _mm(a, None, w_dev=wd)
     # the workload's M, M on both sides of the single-row-tile variants (A
     # loads for rows 0..63, 0..127, all 256), and M that select each tile
-    # (N = 4096: 64 x 64 up to 256, 128 x 64 to 512, 128 x 128 to 1024, then
-    # the main tile; N = 14336: 64 x 64 to 64, 128 x 128 to 256, the main
-    # tile to 1536, then 256 x 256)
+    # (N = 4096: 64 x 32 up to 128, 64 x 64 to 256, 128 x 64 to 512, 128 x 128
+    # to 1024, then the main tile; N = 14336: 64 x 64 to 64, 128 x 128 to 256,
+    # the main tile to 1536, then 256 x 256)
     for m in list(M_SET[:-1]) + [33, 65, 100, 128, 129, 200, 255, 257, 513, 768, 1024, 1025,
                                  1536, 1537]:
         c = _mm(a[:m], None, w_dev=wd)
