@@ -914,7 +914,7 @@ def headline(steps, warmup, ms_step, tflops, comp, cpu, traffic, extras, extras_
     """The one JSON line bench.py prints: the step's headline, its roofline
     and host baseline, the four stages and a summary of the extras (a few KB
     at most; the full record goes to `extras_path`)."""
-    keep = ("ms", "graph_ms", "GB/s", "TFLOP/s", "hbm_frac", "mfma_frac")
+    keep = ("ms", "graph_ms", "GB/s", "TFLOP/s", "hbm_frac", "mfma_frac", "graph_frac")
     line = {
         "metric": METRIC,
         "value": tflops,
@@ -1025,6 +1025,12 @@ def main():
     comp["matmul"]["mfma_frac"] = tflops / MFMA_BF16_PEAK
     comp["attn_prefill"]["mfma_frac"] = comp["attn_prefill"]["TFLOP/s"] / MFMA_BF16_PEAK
     comp["attn_decode"]["hbm_frac"] = comp["attn_decode"]["GB/s"] / HBM_PEAK_GBS
+    # the same fractions from the graph replays (the kernels' own time)
+    for key, unit, peak in (("rmsnorm", "GB/s", HBM_PEAK_GBS), ("matmul", "TFLOP/s", MFMA_BF16_PEAK),
+                            ("attn_prefill", "TFLOP/s", MFMA_BF16_PEAK),
+                            ("attn_decode", "GB/s", HBM_PEAK_GBS)):
+        g = comp[key].get("graph_" + unit)
+        comp[key]["graph_frac"] = g / peak if g else None
     extras = {}
 
     def extra(name, fn):
