@@ -699,8 +699,8 @@ struct StreamSrc {
   static constexpr int STORES = PartialRec<D>::STORES;    // previous unit's record
   static_assert(16 % RING == 0, "slots repeat every split");
   static_assert(LOADS * (AHEAD - 1) + STORES + QLOADS <= 63, "vmcnt range");
-  const uint16_t* kc;
-  const uint16_t* vc;
+  uint16_t* kc;  // written only by append (bf16 cache)
+  uint16_t* vc;
   const uint8_t* ring;
   const ChunkLaneOffs<D>* offs;
   int nkv;
@@ -728,7 +728,7 @@ struct StreamSrc {
     const bool isv = lane >= CPR;
     const u32x4 x = *(lds_u32x4*)(uintptr_t)(stage + (isv ? 1024u : 0u) + 16u * (uint32_t)j);
     if (lane < 2 * CPR) {
-      uint16_t* pool = const_cast<uint16_t*>(isv ? vc : kc);
+      uint16_t* pool = isv ? vc : kc;
       const int64_t row = (((int64_t)un.sp.pg[15] * nkv + un.g) << 4) + (un.last & 15);
       *(u32x4*)(pool + row * D + 8 * j) = x;
     }
@@ -905,9 +905,9 @@ template <int D, int WAVES, int RING, bool Q16>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bi_attn_decode_partial_kernel(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ bt, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, float* __restrict__ ws, int B, int nq, int nkv, int max_pages,
-    int smax, float c2, const float* __restrict__ kf, const float* __restrict__ vf,
+    const int32_t* __restrict__ bt, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    float* __restrict__ ws, int B, int nq, int nkv, int max_pages, int smax, float c2,
+    const float* __restrict__ kf, const float* __restrict__ vf,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
   using Src = StreamSrc<D, RING, Q16>;
   constexpr int QSLOT = 16 * KV<D>::ROWB;
@@ -1535,7 +1535,7 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const void* k_ne
   hipLaunchKernelGGL((bi_attn_decode_partial_kernel<DD, QQ ? kDecodeWaves16 : kDecodeWaves,      \
                                                     QQ ? kDecodeSlots16 : kDecodeSlots, QQ>),    \
                      grid1, dim3(64 * waves), 0, st, (const uint16_t*)q, kv_len, bt,             \
-                     (const uint16_t*)kc, (const uint16_t*)vc, ws, s.B, s.nq, s.nkv, s.max_pages, \
+                     (uint16_t*)kc, (uint16_t*)vc, ws, s.B, s.nq, s.nkv, s.max_pages,           \
                      max_splits, c2, kf, vf, (const uint16_t*)k_new, (const uint16_t*)v_new)
   if (s.d == 128) {
     if (q16)
