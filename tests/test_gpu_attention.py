@@ -138,7 +138,8 @@ def test_decode_batch_companions_and_position():
         assert np.array_equal(r, results[0])
 
 
-def test_decode_append_writes_exactly_the_new_rows():
+@pytest.mark.parametrize("nq,nkv,d", [(32, 8, 128), (8, 2, 64), (4, 4, 64)])
+def test_decode_append_writes_exactly_the_new_rows(nq, nkv, d):
     """The decode call appends its token inside the split pass.  After one
     decode step every pool row is what it was, except each sequence's new
     position, which holds that token's key and value rows bitwise: new
@@ -146,7 +147,7 @@ def test_decode_append_writes_exactly_the_new_rows():
     key), mid-split, 511 and 4095.  Unused pages stay NaN-poisoned."""
     from helpers import bits_of
     lens = [1, 256, 257, 300, 512, 4096]
-    prob = _gqa(lens, seed=11)
+    prob = synth.attn_problem(lens, n_q=nq, n_kv=nkv, d=d, seed=11)
     run = PagedRun(prob, page_seed=4)
     run.prefill([(b, L - 1) for b, L in enumerate(lens) if L > 1])
     k_before, v_before = bits_of(run.kc), bits_of(run.vc)
