@@ -1204,21 +1204,20 @@ struct SplitFactors {
 
 // WAVES waves share the copy: load n of wave w brings keys (WAVES*n + w)*KPI
 // .. +KPI-1, which lie in page (WAVES*n*KPI)/16 + (w*KPI)/16 of the split.
-template <int D, bool IS_K, int WAVES>
-__device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPages& sp, int nkv,
-                                            int g, int key0, int last, uint8_t* lds,
-                                            const StageLaneOffs<D>& offs,
-                                            const SplitFactors& fac = SplitFactors{}) {
-  constexpr int KPI = kWave / KV<D>::CPR;       // keys per 1 KiB load
-  constexpr int NLOAD = 256 / KPI / WAVES;      // loads per thread
+// stage_part issues loads N0 .. N0+CNT-1 of the wave's NLOAD.
+template <int D, int WAVES>
+struct StageGeom {
+  static constexpr int KPI = kWave / KV<D>::CPR;       // keys per 1 KiB load
+  static constexpr int NLOAD = 256 / KPI / WAVES;      // loads per thread
   static_assert((WAVES * KPI) % 16 == 0 && KPI <= 16, "a load stays inside one page");
+};
+template <int D, bool IS_K, int WAVES, int N0, int CNT>
+__device__ __forceinline__ void stage_part(const uint16_t* pool, const SplitPages& sp, int nkv,
+                                           int g, int key0, int last, uint32_t base,
+                                           const StageLaneOffs<D>& offs) {
+  constexpr int KPI = StageGeom<D, WAVES>::KPI;
+  static_assert(N0 >= 0 && CNT >= 0 && N0 + CNT <= StageGeom<D, WAVES>::NLOAD, "load range");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (IS_K && fac.kf != nullptr) {
-    // before the row loads: the block-table read is waited for here, with no
-    // direct load of this stage in flight yet
-    if (wave == 0) stage_factors(fac.kf, fac.bt_row, key0, last, nkv, g, fac.klds);
-    if (wave == 1) stage_factors(fac.vf, fac.bt_row, key0, last, nkv, g, fac.vlds);
-  }
   const int poff = (wave * KPI) >> 4;           // pages the wave's first key is past
   auto page_of = [&](int pidx) __attribute__((always_inline)) {
     if constexpr (WAVES * KPI <= 32) {           // poff is 0 or 1
@@ -1229,12 +1228,11 @@ __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPag
       return poff & 2 ? b : a;
     }
   };
-  const uint32_t base = (uint32_t)(uintptr_t)lds;
   if (key0 + kSplit - 1 <= last) {
     const uint16_t* pool_g = pool + (int64_t)g * 16 * D;
     const uint32_t page_elems = (uint32_t)nkv * 16 * D;
     const uint32_t wbase = base + (uint32_t)(wave * KPI * KV<D>::ROWB);
-    static_for<0, NLOAD>([&](auto nc) {
+    static_for<N0, N0 + CNT>([&](auto nc) {
       constexpr int n = decltype(nc)::value;
       constexpr int pidx = (n * WAVES * KPI) >> 4;
       constexpr int h = ((n * WAVES * KPI) >> 4) & 1;
@@ -1244,13 +1242,61 @@ __device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPag
     return;
   }
 #pragma unroll
-  for (int n = 0; n < NLOAD; ++n) {
+  for (int n = N0; n < N0 + CNT; ++n) {
     const int pidx = (n * WAVES * KPI) >> 4;    // compile-time after unrolling
     const int kfirst = (n * WAVES + wave) * KPI;
     dma_block<D, IS_K>(pool, page_of(pidx), nkv, g, key0, kfirst, last,
                        base + (uint32_t)kfirst * KV<D>::ROWB);
   }
 }
+
+template <int D, bool IS_K, int WAVES>
+__device__ __forceinline__ void stage_split(const uint16_t* pool, const SplitPages& sp, int nkv,
+                                            int g, int key0, int last, uint8_t* lds,
+                                            const StageLaneOffs<D>& offs,
+                                            const SplitFactors& fac = SplitFactors{}) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (IS_K && fac.kf != nullptr) {
+    // before the row loads: the block-table read is waited for here, with no
+    // direct load of this stage in flight yet
+    if (wave == 0) stage_factors(fac.kf, fac.bt_row, key0, last, nkv, g, fac.klds);
+    if (wave == 1) stage_factors(fac.vf, fac.bt_row, key0, last, nkv, g, fac.vlds);
+  }
+  stage_part<D, IS_K, WAVES, 0, StageGeom<D, WAVES>::NLOAD>(pool, sp, nkv, g, key0, last,
+                                                          (uint32_t)(uintptr_t)lds, offs);
+}
+
+// The bf16 prefill source with the stage loads spread over the chunks: the
+// value rows of split s are issued over the first STEPS 32-key chunks of its
+// logits, the key rows of split s+1 over the first STEPS chunks of its
+// weighted sum (which start once every wave is past the barrier that frees
+// the buffer), so that the memory pipe works beside the MFMAs instead of
+// holding every wave at one burst of loads.  Issuing them all at the first
+// chunk, or spreading them over four or eight, measured slower than two.
+template <int D, int WAVES, int STEPS>
+struct SpreadSrc : StagedSrc<D> {
+  static constexpr int NLOAD = StageGeom<D, WAVES>::NLOAD;
+  static constexpr int NSTEP = STEPS < NLOAD ? STEPS : NLOAD;
+  static constexpr int PER = NLOAD / NSTEP;
+  static_assert(PER * NSTEP == NLOAD, "loads per step");
+  const uint16_t* kc;
+  const uint16_t* vc;
+  SplitPages vpages, kpages;
+  int nkv, g, vkey0, kkey0, last;
+  bool kon;
+  uint32_t klds, vlds;
+  const StageLaneOffs<D>* offs;
+  template <int IDX>
+  __device__ __forceinline__ void step() const {
+    constexpr int c = IDX % 8;
+    if constexpr (c < NSTEP) {
+      if constexpr (IDX < 8)
+        stage_part<D, false, WAVES, c * PER, PER>(vc, vpages, nkv, g, vkey0, last, vlds, *offs);
+      else if (kon)
+        stage_part<D, true, WAVES, c * PER, PER>(kc, kpages, nkv, g, kkey0, last, klds, *offs);
+    }
+  }
+};
 
 // Q16: the cache holds int16 rows with per-(page, kv head, slot) factors
 // kf / vf (nullptr otherwise).  cu_q == nullptr means one token per sequence.
@@ -1297,7 +1343,8 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_prefill_kernel(
   const int pmin = start + tile * per_wg + wave * NB * ppb;
   const int nsplit = pmax / kSplit + 1;
   const int32_t* bt_row = bt + (int64_t)b * max_pages;
-  using Src = std::conditional_t<Q16, StagedSrc16<D>, StagedSrc<D>>;
+  constexpr int kSpreadSteps = 2;
+  using Src = std::conditional_t<Q16, StagedSrc16<D>, SpreadSrc<D, WAVES, kSpreadSteps>>;
   Src src;
   src.ol.init((uint32_t)(uintptr_t)klds, (uint32_t)(uintptr_t)vlds);
   SplitFactors fac;
@@ -1321,13 +1368,30 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_prefill_kernel(
   StageLaneOffs<D> soffs;
   soffs.init(wave);
   stage_split<D, true, WAVES>(kc, pages, nkv, g, 0, L - 1, klds, soffs, fac);
+  if constexpr (!Q16) {
+    src.kc = kc;
+    src.vc = vc;
+    src.nkv = nkv;
+    src.g = g;
+    src.last = L - 1;
+    src.klds = (uint32_t)(uintptr_t)klds;
+    src.vlds = (uint32_t)(uintptr_t)vlds;
+    src.offs = &soffs;
+  }
   for (int s = 0; s < nsplit; ++s) {
     const int key0 = s * kSplit;
     wait_vmcnt_le<0>();
     __syncthreads();  // K(s) in LDS; every wave is done reading V(s-1)
-    stage_split<D, false, WAVES>(vc, pages, nkv, g, key0, L - 1, vlds, soffs);
+    if constexpr (Q16) stage_split<D, false, WAVES>(vc, pages, nkv, g, key0, L - 1, vlds, soffs);
     SplitPages next;  // the next split's pages, fetched while this one computes
     if (s + 1 < nsplit) next.load(bt_row, key0 + kSplit, L - 1);
+    if constexpr (!Q16) {
+      src.vpages = pages;
+      src.vkey0 = key0;
+      src.kpages = next;
+      src.kkey0 = key0 + kSplit;
+      src.kon = s + 1 < nsplit;
+    }
     u32x4 p[NB][8];
     float ms[NB], ls[NB];
     split_qk<D, NB>(src, key0, INT_MAX, pmin, qf, pcol, c2, p, ms, ls);
@@ -1335,7 +1399,8 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_prefill_kernel(
     __syncthreads();  // V(s) in LDS; every wave is done reading K(s)
     if (s + 1 < nsplit) {
       pages = next;
-      stage_split<D, true, WAVES>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs, fac);
+      if constexpr (Q16)
+        stage_split<D, true, WAVES>(kc, pages, nkv, g, key0 + kSplit, L - 1, klds, soffs, fac);
     }
     f32x4 os[NB][DB];
     split_pv<D, NB>(src, p, os);
