@@ -1313,8 +1313,15 @@ __global__ __launch_bounds__(64 * WAVES) void bi_attn_prefill_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t flds[Q16 ? 2 * 1024 : 16];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int tile = (int)(gridDim.x - 1 - blockIdx.x);
+  // the workgroups of one (sequence, kv head) go to one XCD, whose L2 then
+  // serves each split's rows to all of them; tiles in descending order, so
+  // that the longest start first
+  const uint32_t nwg = gridDim.x * gridDim.y * gridDim.z;
+  const uint32_t lid =
+      xcd_contiguous_id(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), nwg);
+  const uint32_t lrest = lid / gridDim.x;
+  const int b = (int)(lrest / gridDim.y), g = (int)(lrest % gridDim.y);
+  const int tile = (int)(gridDim.x - 1 - lid % gridDim.x);
   const int group = nq / nkv;
   const int ppb = 16 / group;  // positions per block
   const int per_wg = WAVES * NB * ppb;
