@@ -687,8 +687,9 @@ def _timed(run, units, target_s, max_n=None):
 def cpu_oracle(wl, target_s=3.0):
     """The oracle on the host, on all cores and on one, in the GPU side's
     units: the matmul (TFLOP/s over rows of A x the full W), RMSNorm (GB/s over
-    rows of x) and decode attention (GB/s over sequences of the decode batch,
-    keys and values gathered from the paged pool)."""
+    rows of x), decode attention (GB/s over sequences of the decode batch,
+    keys and values gathered from the paged pool) and the prefill chunk
+    (TFLOP/s over its queries, each against its own causal prefix)."""
     import numpy as np
     import oracle
     torch = wl.torch
@@ -728,6 +729,26 @@ def cpu_oracle(wl, target_s=3.0):
             decode(min(n - s, B_DEC))
 
     kv_bytes = lambda n: sum(wl.dec_lens[i % B_DEC] for i in range(n)) * NKV * D * 4 / 1e9
+
+    # the prefill chunk: its sequence's keys and values (the chunk's own rows
+    # are in the pool once a step has run) and its queries at positions
+    # pre_len - 512 .. pre_len - 1
+    Lp = wl.pre_len
+    pos0 = Lp - PREFILL_CHUNK
+    pages_pre = bt[B_DEC, :(Lp + 15) // 16]
+    k_pre = np.ascontiguousarray(kc[pages_pre].transpose(0, 2, 1, 3).reshape(-1, NKV, D)[:Lp])
+    v_pre = np.ascontiguousarray(vc[pages_pre].transpose(0, 2, 1, 3).reshape(-1, NKV, D)[:Lp])
+    q_pre = wl.q_pre.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def prefill(n):
+        # the chunk's first n queries, in passes over the chunk
+        for s in range(0, n, PREFILL_CHUNK):
+            m = min(n - s, PREFILL_CHUNK)
+            oracle.attention(q_pre[:m], k_pre, v_pre, [Lp], [0] * m, list(range(pos0, pos0 + m)),
+                             wl.scale, threads=threads)
+
+    pre_flops = lambda n: sum(4.0 * D * NQ * (pos0 + i % PREFILL_CHUNK + 1)
+                              for i in range(n)) / 1e12
     out = {"cores": oracle.default_threads(), "model": _cpu_model(), "kind": "oracle"}
     for label, threads in (("all_cores", oracle.default_threads()), ("one_core", 1)):
         r = {}
@@ -739,6 +760,8 @@ def cpu_oracle(wl, target_s=3.0):
         r["rmsnorm_GB/s"] = {"value": v, "rows": n, "s": dt}
         n, v, dt = _timed(decode_seqs, kv_bytes, target_s)
         r["decode_GB/s"] = {"value": v, "sequences": n, "s": dt}
+        n, v, dt = _timed(prefill, pre_flops, target_s)
+        r["prefill_TFLOP/s"] = {"value": v, "queries": n, "s": dt}
         out[label] = r
     return out
 
