@@ -26,8 +26,12 @@
 // four k rows a 32-lane half reads fall on four different block positions and
 // every transposing read is conflict-free.
 //
-// Schedule: one barrier per k-tile, placed before the last k-step of k-tile
-// k, publishes k-tile k+1 and frees k-tile k's stage.  Fragments of every
+// Schedule of the 256 x 256 tile: the two wave rows of the workgroup (one
+// wave of each per SIMD) take turns, one phase apart: while one reads a
+// k-tile's fragments from LDS and issues loads, the other runs its MFMAs on
+// the fragments it read in the phase before, at raised issue priority.
+// Schedule of the other tiles: one barrier per k-tile, placed before the last
+// k-step of k-tile k, publishes k-tile k+1 and frees k-tile k's stage.  Fragments of every
 // k-step are read while the previous step's MFMAs run (across the barrier
 // too), and the refill loads are issued in small groups after the MFMAs of
 // each k-step, so the vector memory unit never holds up a wave that has MFMAs
@@ -58,10 +62,14 @@
 namespace bi {
 namespace {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = kMatmulBK>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = kMatmulBK,
+          int PP_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_,
                        STAGES = STAGES_;
+  // PP: the two halves of the workgroup take turns (1; 2 also raises the
+  // issuing priority of the half in its MFMA phase)
+  static constexpr int PP = PP_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 32, NI = WN / 32;
   static constexpr int KS = BK / 16;                  // MFMA k-steps per k-tile
@@ -89,15 +97,17 @@ struct TileCfg {
   // the single-row-tile variants (live row blocks, fewer A loads) need two
   // 32-row blocks per wave and A load i filling rows 64i .. 64i+63
   static constexpr bool LIVE_VARIANTS = MI == 2 && A_LOADS == 4 && BM / A_LOADS == 64;
+  static_assert(PP == 0 || (!LIVE_VARIANTS && WAVES_M == 2 && WAVES_N == 4 && STAGES >= 3),
+                "the alternating halves are the two wave rows");
 };
 // The main tile, a larger one for launches with at least a round of them,
 // and four smaller ones for launches whose main-tile grid would leave CUs
 // idle: 256 x 256 (eight 128 x 64 waves; 32-wide k-tiles, so that four stages
-// fit), 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64 (four 64 x 32
+// fit; its wave rows alternate MFMA and memory phases), 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64 (four 64 x 32
 // waves), 64 x 64 (four 32 x 32 waves) and 64 x 32 (two 32 x 32 waves, twice
 // the workgroups on W of a small-M launch).
 using Tile = TileCfg<256, 128, 4, 2, 3>;
-using TileL = TileCfg<256, 256, 2, 4, 4, 32>;
+using TileL = TileCfg<256, 256, 2, 4, 4, 32, 2>;
 using TileM = TileCfg<128, 128, 2, 2, 3>;
 using TileN = TileCfg<128, 64, 2, 2, 4>;
 using TileS = TileCfg<64, 64, 2, 2, 4>;
@@ -497,7 +507,79 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
         run(std::integral_constant<int, 0>{}, nc);
     }
   };
-  if constexpr (SPLIT || !T::LIVE_VARIANTS) {  // the comparator keeps the one full ring
+  // Alternating halves (T::PP).  Wave w runs on SIMD w mod 4, so each SIMD
+  // holds one wave of each wave row: half 0 (rows 0..BM/2-1) and half 1.  A
+  // wave alternates a memory phase (read the whole k-tile's fragments, issue
+  // its loads of the k-tile R-1 ahead) and an MFMA phase on those fragments,
+  // one barrier after each; half 1 runs one phase behind half 0, so while one
+  // wave of a SIMD issues its MFMAs the other reads LDS and loads.  Phase
+  // slots: half 0 reads k-tile j in slot 2j-1 and multiplies in 2j; half 1
+  // reads in 2j and multiplies in 2j+1.  So k-tile j's stage is free from slot
+  // 2j+1, when the loads of k-tile j+R-1 go out into it (half 0 in 2j+1, half
+  // 1 in 2j+2), and each wave waits for its own loads of k-tile j+1 before the
+  // barrier that ends slot 2j (half 0 after its MFMA phase, half 1 after its
+  // memory phase): R-2 later k-tiles of its loads may still be in flight.
+  // Every element sees the same MFMAs in the same k order as in the other
+  // tiles; only the issue order across the halves changes.
+  auto run_pp = [&]() __attribute__((always_inline)) {
+    constexpr int NA = T::A_LOADS, LOADS = NA + T::W_LOADS, R = STAGES;
+    static_assert((R - 2) * LOADS <= 63, "vmcnt range");
+    constexpr auto nc = std::integral_constant<int, NA>{};
+    constexpr auto all = std::integral_constant<int, MI>{};
+    const bool half1 = wave_m != 0;
+    bf16x8 pa[KS][MI], pb[KS][NI];
+    auto slot_pair = [&](auto sc) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      // memory phase
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) frags_n(smem + S * STAGE, kk, pa[kk], pb[kk], all, nc);
+      issue((S + R - 1) % R, 0, LOADS, nc);
+      advance();
+      if (half1) wait_vmcnt_le<(R - 2) * LOADS>();
+      lds_reads_done();
+      __syncthreads();
+      // MFMA phase
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (T::PP == 2) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = mfma32(pa[kk][mi], pb[kk][ni], acc[mi][ni]);
+      if constexpr (T::PP == 2) __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (++ckt == nk) {  // the tile is complete
+        store_tile(cm0, cn0, acc);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
+        ckt = 0;
+        if (++ct < count) raster_tile<T>(first + ct * step, tiles_m, tiles_n, cm0, cn0);
+      }
+      if (!half1) wait_vmcnt_le<(R - 2) * LOADS>();
+      __syncthreads();
+    };
+#pragma unroll
+    for (int s = 0; s < R - 1; ++s) {
+      issue(s, 0, LOADS, nc);
+      advance();
+    }
+    wait_vmcnt_le<(R - 2) * LOADS>();
+    __syncthreads();
+    if (half1) __syncthreads();  // half 1 starts one phase behind
+    int64_t p = 0;
+    for (; p + R <= total; p += R) static_for<0, R>(slot_pair);
+    static_for<0, R - 1>([&](auto sc) __attribute__((always_inline)) {
+      if (p + decltype(sc)::value < total) slot_pair(sc);
+    });
+    if (!half1) __syncthreads();  // as many barriers as half 1
+  };
+  if constexpr (T::PP != 0 && !SPLIT) {
+    run_pp();
+  } else if constexpr (SPLIT || !T::LIVE_VARIANTS) {  // the comparator keeps the one full ring
     run_live(std::integral_constant<int, T::A_LOADS>{});
   } else {
     if (na == 1)
