@@ -28,6 +28,8 @@
  *     other entry point is reentrant.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
  *     Inputs must stay alive and unmodified until that work completes.
+ *   - Every call but bi_abi_version and the *_bytes queries returns a
+ *     bi_status (an int-sized enum).
  *   - Host arguments are checked before anything is enqueued.  On any non-OK
  *     status nothing has been enqueued.  Kernel faults surface, as usual in
  *     HIP, at the caller's next synchronisation.
@@ -94,7 +96,7 @@ const char* bi_status_string(int status);
  * waves' partials added in wave order.
  * Requires hidden % 8 == 0 and 8 <= hidden <= 16384 (else BI_ERR_UNSUPPORTED).
  */
-int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+bi_status bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
                int64_t hidden, float eps, void* stream);
 
 /* ------------------------------------------------------------------------- */
@@ -115,13 +117,13 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t r
  * Requires k % 64 == 0, n % 8 == 0, k <= 2^22 and n <= 2^24 (else
  * BI_ERR_UNSUPPORTED).
  */
-int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
+bi_status bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
               void* stream);
 
 /* The output tile bi_matmul uses for an m x n product on the current device
  * (tile_m x tile_n) and the workgroups it launches.  Host-only; any pointer
  * may be NULL.  BI_ERR_INVALID_SHAPE for m or n < 1. */
-int bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups);
+bi_status bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups);
 
 /* ------------------------------------------------------------------------- */
 /* Paged attention (approach table, Attention row: one unified cache layout,
@@ -176,7 +178,7 @@ size_t bi_attn_workspace_bytes(const bi_attn_shape* s, int64_t num_tokens, int32
  *   max_q_per_seq (host) >= every n_b, used to size the grid.
  * Requires n_b <= kv_len[b] <= max_pages_per_seq * page_size (trusted).
  * No workspace. */
-int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+bi_status bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                     const int32_t* cu_q, const int32_t* kv_len, const int32_t* block_table,
                     void* k_cache, void* v_cache, void* out, float* lse, int64_t total_q,
                     int32_t max_q_per_seq, void* stream);
@@ -193,7 +195,7 @@ int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, co
  * unwritten and its outputs undefined.
  *   workspace: device, >= bi_attn_workspace_bytes(s, B, max_kv_len) bytes,
  *   contents on entry ignored, scratch for the per-split partials. */
-int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+bi_status bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                    const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                    void* v_cache, void* out, float* lse, int32_t max_kv_len, void* workspace,
                    size_t workspace_bytes, void* stream);
@@ -215,7 +217,7 @@ int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, con
  *   from different threads -- race and must be ordered by the caller.
  *   The debug library does not check the index arrays for this call. */
 #define BI_DECODE_SCRATCH_BYTES (64u << 20)
-int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_new,
+bi_status bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_new,
                            const void* v_new, const int32_t* kv_len, const int32_t* block_table,
                            void* k_cache, void* v_cache, void* out, float* lse,
                            int32_t max_kv_len, void* stream);
@@ -229,7 +231,7 @@ int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_
  * bix_rmsnorm_splitrow: each row's sum of squares is split over `chunks`
  * workgroups (chunks <= 0: chosen from `rows`, more chunks for fewer rows),
  * partials added by a second kernel.  workspace >= rows * 64 * 4 bytes. */
-int bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+bi_status bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
                          int64_t hidden, float eps, int32_t chunks, void* workspace,
                          size_t workspace_bytes, void* stream);
 
@@ -240,7 +242,7 @@ int bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd,
  * is bi_matmul (no workspace is touched).  workspace >=
  * bix_matmul_workspace_bytes. */
 size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split_k);
-int bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
+bi_status bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
                       int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                       void* stream);
 
@@ -250,7 +252,7 @@ int bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_
  * bix_attn_decode_workspace_bytes. */
 size_t bix_attn_decode_workspace_bytes(const bi_attn_shape* s, int32_t max_kv_len,
                                        int32_t num_splits);
-int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k_new,
+bi_status bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k_new,
                             const void* v_new, const int32_t* kv_len, const int32_t* block_table,
                             void* k_cache, void* v_cache, void* out, float* lse,
                             int32_t max_kv_len, int32_t num_splits, void* workspace,
@@ -264,14 +266,14 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
  * inputs as in a matmul (the pipe's power, and so the clock the chip holds,
  * depends on the bits); 0: one fixed, smooth pair.  sink: device float,
  * written never (it only keeps the work from being optimised away). */
-int bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink, void* stream);
+bi_status bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink, void* stream);
 
 /* bix_read_stream: measurement only, the HBM read ceiling.  Reads `bytes`
  * (a multiple of 8192) from device pointer p (16-byte aligned) once, as 8 KiB
  * chunks streamed through LDS by direct loads (the decode kernel's way of
  * reading), from `workgroups` workgroups of two waves.  sink: device uint32,
  * written never.  INVALID_SHAPE for a misaligned pointer or size. */
-int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
+bi_status bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
                     void* stream);
 
 /* ---- Decoder-stack element-wise operations ---------------------------------
@@ -288,7 +290,7 @@ int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* 
 /* out[t, :] = table[ids[t], :].  ids int32 [tokens] (device; entries outside
  * [0, vocab) are clamped into it); table bf16 [vocab, hidden]; out bf16
  * [tokens, hidden].  hidden % 8 == 0.  Also a plain row gather. */
-int bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, int64_t hidden,
+bi_status bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, int64_t hidden,
              int64_t vocab, void* stream);
 
 /* Rotary position embedding in place, "rotate half" pairing: for token t at
@@ -298,12 +300,12 @@ int bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, i
  *   x[i] = bf16(a cos - b sin),  x[i + head_dim/2] = bf16(a sin + b cos).
  * head_dim even and <= 256; theta > 1.  q or k may be NULL when n_q or n_kv
  * is 0.  pos int32 [tokens] (device). */
-int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, int32_t n_kv,
+bi_status bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, int32_t n_kv,
             int32_t head_dim, float theta, void* stream);
 
 /* out = bf16(silu(gate) * up) element-wise, silu(g) = g / (1 + e^-g) in fp32.
  * gate, up, out bf16 [n], n % 8 == 0; out may alias gate or up. */
-int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream);
+bi_status bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream);
 
 /* The output of one fused q|k|v projection split into the q, k and v tensors
  * the attention calls take, with bi_rope's rotation (the same arithmetic)
@@ -314,22 +316,22 @@ int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stre
  * projection (one bi_matmul against [W_q | W_k | W_v]) gives every column the
  * bits of the separate ones: a column's dot product does not depend on its
  * neighbours. */
-int bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, int64_t tokens,
+bi_status bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, int64_t tokens,
                 int32_t n_q, int32_t n_kv, int32_t head_dim, float theta, void* stream);
 
 /* bi_swiglu over the output of one fused gate|up projection: gu bf16
  * [rows, 2f] (row r: gate, then up), out bf16 [rows, f] not overlapping gu;
  * f % 8 == 0. */
-int bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* stream);
+bi_status bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* stream);
 
 /* out = bf16(a + b) element-wise (the residual add).  bf16 [n], n % 8 == 0;
  * out may alias a or b. */
-int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
+bi_status bi_add(const void* a, const void* b, void* out, int64_t n, void* stream);
 
 /* Greedy sampling: out[r] = the index of the largest of x[r, 0..n-1] (fp32
  * [rows, n], 4-byte aligned), the lowest such index on ties.  NaN is never
  * chosen; a row holding no number gives 0.  out int32 [rows]. */
-int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream);
+bi_status bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream);
 
 /* ---- Int16 KV cache ----------------------------------------------------------
  * The HEAL page on gist.science (its new-solution section, item 1) packs the
@@ -352,7 +354,7 @@ int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* strea
  * Inputs must be finite. */
 
 /* As bi_attn_prefill, with the int16 caches and their factor arrays. */
-int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,
+bi_status bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,
                         const void* v_new, const int32_t* cu_q, const int32_t* kv_len,
                         const int32_t* block_table, void* k_cache, void* v_cache, float* k_scale,
                         float* v_scale, void* out, float* lse, int64_t total_q,
@@ -363,7 +365,7 @@ int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new
  * partials (the decode kernel, each unit's 256 key and value factors staged
  * with its q) and the fixed-order fold.  max_kv_len, workspace and
  * workspace_bytes as in bi_attn_decode (bi_attn_workspace_bytes sizes it). */
-int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+bi_status bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                        const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                        void* v_cache, float* k_scale, float* v_scale, void* out, float* lse,
                        int32_t max_kv_len, void* workspace, size_t workspace_bytes,
@@ -387,7 +389,7 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
 
 /* W3 = [hi(w); lo(w); hi(w)]: w fp32 [k, n] -> w3 bf16 [3k, n] (a weight is
  * packed once). */
-int bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream);
+bi_status bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream);
 
 /* Bytes of workspace bi_matmul_ec needs for any operand type: m * 3k * 2
  * (the packed A3; a bf16 a needs only m * 2k * 2). */
@@ -408,7 +410,7 @@ size_t bi_matmul_ec_workspace_bytes(int64_t m, int64_t k);
  *   nearest even, as bi_matmul's bf16 output).
  * k % 64 == 0, n % 8 == 0, 3k <= 2^22 (else BI_ERR_UNSUPPORTED).  workspace:
  * device, >= m * K' * 2 bytes.  Rows are invariant as bi_matmul's are. */
-int bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtype, int64_t m,
+bi_status bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtype, int64_t m,
                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus

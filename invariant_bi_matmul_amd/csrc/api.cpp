@@ -25,7 +25,7 @@ namespace {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
+bi_status hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
 constexpr int64_t kMaxGridX = 0x7fffffff;
 constexpr int64_t kMaxGridYZ = 65535;
@@ -79,7 +79,7 @@ int debug_check_tables(const bi_attn_shape* s, const int32_t* kv_len, const int3
 #define BI_CHECK_TABLES(...)                          \
   do {                                                \
     const int chk = debug_check_tables(__VA_ARGS__); \
-    if (chk != BI_OK) return chk;                     \
+    if (chk != BI_OK) return (bi_status)chk;         \
   } while (0)
 #else
 #define BI_CHECK_TABLES(...) \
@@ -124,12 +124,12 @@ static int check_rmsnorm(const void* x, const void* gamma, void* y, float* rstd,
   return BI_OK;
 }
 
-int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+bi_status bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
                int64_t hidden, float eps, void* stream) {
   try {
     const int c = check_rmsnorm(x, gamma, y, rstd, rows, hidden);
     if (c < 0) return BI_OK;
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     if (!(eps >= 0.0f) || !isfinite(eps)) return BI_ERR_INVALID_SHAPE;
     return hip_status(
         bi::launch_rmsnorm(x, gamma, y, rstd, rows, (int)hidden, eps, (hipStream_t)stream));
@@ -138,13 +138,13 @@ int bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int64_t r
   }
 }
 
-int bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
+bi_status bix_rmsnorm_splitrow(const void* x, const void* gamma, void* y, float* rstd, int64_t rows,
                          int64_t hidden, float eps, int32_t chunks, void* workspace,
                          size_t workspace_bytes, void* stream) {
   try {
     const int c = check_rmsnorm(x, gamma, y, rstd, rows, hidden);
     if (c < 0) return BI_OK;
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     if (!(eps >= 0.0f) || !isfinite(eps)) return BI_ERR_INVALID_SHAPE;
     if (chunks <= 0) chunks = bi::rmsnorm_splitrow_auto_chunks(rows);
     if (chunks > 64 || chunks > hidden / 8) return BI_ERR_UNSUPPORTED;
@@ -175,12 +175,12 @@ static int check_matmul(const void* a, const void* w, void* c, int c_dtype, int6
   return BI_OK;
 }
 
-int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
+bi_status bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
               void* stream) {
   try {
     const int s = check_matmul(a, w, c, c_dtype, m, n, k);
     if (s < 0) return BI_OK;
-    if (s != BI_OK) return s;
+    if (s != BI_OK) return (bi_status)s;
     return hip_status(
         bi::launch_matmul(a, w, c, c_dtype == BI_DTYPE_F32, m, n, k, (hipStream_t)stream));
   } catch (...) {
@@ -188,7 +188,7 @@ int bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int
   }
 }
 
-int bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups) {
+bi_status bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups) {
   if (m < 1 || n < 1) return BI_ERR_INVALID_SHAPE;
   int bm, bn;
   int64_t grid;
@@ -206,13 +206,13 @@ size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split
   return (size_t)split_k * (size_t)m * (size_t)n * sizeof(float);
 }
 
-int bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
+bi_status bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
                       int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                       void* stream) {
   try {
     const int s = check_matmul(a, w, c, c_dtype, m, n, k);
     if (s < 0) return BI_OK;
-    if (s != BI_OK) return s;
+    if (s != BI_OK) return (bi_status)s;
     if (k == 0) return BI_ERR_UNSUPPORTED;
     if (split_k <= 0) split_k = bi::matmul_splitk_auto(m, n, k);
     if (split_k > k / bi::kMatmulBK || split_k > 65535) return BI_ERR_UNSUPPORTED;
@@ -234,13 +234,13 @@ size_t bi_attn_workspace_bytes(const bi_attn_shape* s, int64_t num_tokens, int32
   return decode_ws_bytes(s, num_tokens, ns > 0 ? ns : 1);
 }
 
-int bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+bi_status bi_attn_prefill(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                     const int32_t* cu_q, const int32_t* kv_len, const int32_t* block_table,
                     void* k_cache, void* v_cache, void* out, float* lse, int64_t total_q,
                     int32_t max_q_per_seq, void* stream) {
   try {
     const int c = check_attn_shape(s);
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     if (total_q < 0 || max_q_per_seq < 0) return BI_ERR_INVALID_SHAPE;
     if (s->num_seqs == 0 || total_q == 0 || max_q_per_seq == 0) return BI_OK;
     if (max_q_per_seq > total_q) return BI_ERR_INVALID_SHAPE;
@@ -271,7 +271,7 @@ static int check_decode(const bi_attn_shape* s, const void* q, const void* k_new
                         void* k_cache, void* v_cache, void* out, float* lse, int32_t max_kv_len,
                         void* workspace) {
   const int c = check_attn_shape(s);
-  if (c != BI_OK) return c;
+  if (c != BI_OK) return (bi_status)c;
   if (max_kv_len < 0) return BI_ERR_INVALID_SHAPE;
   if (s->num_seqs == 0) return -1;
   if (max_kv_len < 1 || max_kv_len > (int64_t)s->max_pages_per_seq * s->page_size)
@@ -286,7 +286,7 @@ static int check_decode(const bi_attn_shape* s, const void* q, const void* k_new
   return BI_OK;
 }
 
-int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+bi_status bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                    const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                    void* v_cache, void* out, float* lse, int32_t max_kv_len, void* workspace,
                    size_t workspace_bytes, void* stream) {
@@ -294,7 +294,7 @@ int bi_attn_decode(const bi_attn_shape* s, const void* q, const void* k_new, con
     const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
                                max_kv_len, workspace);
     if (c < 0) return BI_OK;
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     const int ns = (max_kv_len + bi::kSplit - 1) / bi::kSplit;
     if (workspace_bytes < decode_ws_bytes(s, s->num_seqs, ns)) return BI_ERR_WORKSPACE_TOO_SMALL;
     if ((int64_t)s->num_seqs * s->num_kv_heads * ns / 4 + 1 > kMaxGridX) return BI_ERR_UNSUPPORTED;
@@ -337,7 +337,7 @@ float* scratch_for_current_device() {
 }
 }  // namespace
 
-int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_new,
+bi_status bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_new,
                            const void* v_new, const int32_t* kv_len, const int32_t* block_table,
                            void* k_cache, void* v_cache, void* out, float* lse,
                            int32_t max_kv_len, void* stream) {
@@ -346,7 +346,7 @@ int bi_attn_decode_noalloc(const bi_attn_shape* s, const void* q, const void* k_
     const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
                                max_kv_len, (void*)k_cache);
     if (c < 0) return BI_OK;
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     const int ns = (max_kv_len + bi::kSplit - 1) / bi::kSplit;
     if (decode_ws_bytes(s, s->num_seqs, ns) > (size_t)BI_DECODE_SCRATCH_BYTES)
       return BI_ERR_WORKSPACE_TOO_SMALL;
@@ -372,7 +372,7 @@ size_t bix_attn_decode_workspace_bytes(const bi_attn_shape* s, int32_t max_kv_le
   return decode_ws_bytes(s, s->num_seqs, ns);
 }
 
-int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k_new,
+bi_status bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k_new,
                             const void* v_new, const int32_t* kv_len, const int32_t* block_table,
                             void* k_cache, void* v_cache, void* out, float* lse,
                             int32_t max_kv_len, int32_t num_splits, void* workspace,
@@ -381,7 +381,7 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
     const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
                                max_kv_len, workspace);
     if (c < 0) return BI_OK;
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     if (num_splits <= 0)
       num_splits = bi::attn_splitkv_auto(s->num_seqs, s->num_kv_heads, max_kv_len);
     if (num_splits > max_kv_len) return BI_ERR_UNSUPPORTED;
@@ -403,7 +403,7 @@ int bix_attn_decode_splitkv(const bi_attn_shape* s, const void* q, const void* k
 
 // ---- decoder-stack element-wise operations -----------------------------------
 
-int bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, int64_t hidden,
+bi_status bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, int64_t hidden,
              int64_t vocab, void* stream) {
   try {
     if (tokens < 0 || hidden < 0 || vocab < 0) return BI_ERR_INVALID_SHAPE;
@@ -418,7 +418,7 @@ int bi_embed(const int32_t* ids, const void* table, void* out, int64_t tokens, i
   }
 }
 
-int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, int32_t n_kv,
+bi_status bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, int32_t n_kv,
             int32_t head_dim, float theta, void* stream) {
   try {
     if (tokens < 0 || n_q < 0 || n_kv < 0) return BI_ERR_INVALID_SHAPE;
@@ -436,7 +436,7 @@ int bi_rope(void* q, void* k, const int32_t* pos, int64_t tokens, int32_t n_q, i
   }
 }
 
-int bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, int64_t tokens,
+bi_status bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, int64_t tokens,
                 int32_t n_q, int32_t n_kv, int32_t head_dim, float theta, void* stream) {
   try {
     if (tokens < 0 || n_q <= 0 || n_kv <= 0) return BI_ERR_INVALID_SHAPE;
@@ -454,7 +454,7 @@ int bi_qkv_rope(const void* qkv, const int32_t* pos, void* q, void* k, void* v, 
   }
 }
 
-int bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* stream) {
+bi_status bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* stream) {
   try {
     if (rows < 0 || f < 0 || f % 8 != 0) return BI_ERR_INVALID_SHAPE;
     if (rows == 0 || f == 0) return BI_OK;
@@ -466,7 +466,7 @@ int bi_swiglu_pair(const void* gu, void* out, int64_t rows, int64_t f, void* str
   }
 }
 
-int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream) {
+bi_status bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stream) {
   try {
     if (n < 0 || n % 8 != 0) return BI_ERR_INVALID_SHAPE;
     if (n == 0) return BI_OK;
@@ -478,7 +478,7 @@ int bi_swiglu(const void* gate, const void* up, void* out, int64_t n, void* stre
   }
 }
 
-int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
+bi_status bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
   try {
     if (n < 0 || n % 8 != 0) return BI_ERR_INVALID_SHAPE;
     if (n == 0) return BI_OK;
@@ -492,7 +492,7 @@ int bi_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
 
 // ---- measurement ---------------------------------------------------------------
 
-int bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink, void* stream) {
+bi_status bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink, void* stream) {
   try {
     if (iters < 0 || workgroups < 0) return BI_ERR_INVALID_SHAPE;
     if (iters == 0 || workgroups == 0) return BI_OK;
@@ -505,7 +505,7 @@ int bix_mfma_loop(int64_t iters, int32_t workgroups, int32_t varied, float* sink
   }
 }
 
-int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
+bi_status bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* sink,
                     void* stream) {
   try {
     if (bytes < 0 || workgroups < 0 || bytes % 8192 != 0) return BI_ERR_INVALID_SHAPE;
@@ -520,14 +520,14 @@ int bix_read_stream(const void* p, int64_t bytes, int32_t workgroups, uint32_t* 
 
 // ---- int16 KV cache -----------------------------------------------------------
 
-int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,
+bi_status bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new,
                         const void* v_new, const int32_t* cu_q, const int32_t* kv_len,
                         const int32_t* block_table, void* k_cache, void* v_cache, float* k_scale,
                         float* v_scale, void* out, float* lse, int64_t total_q,
                         int32_t max_q_per_seq, void* stream) {
   try {
     const int c = check_attn_shape(s);
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     if (total_q < 0 || max_q_per_seq < 0) return BI_ERR_INVALID_SHAPE;
     if (s->num_seqs == 0 || total_q == 0 || max_q_per_seq == 0) return BI_OK;
     if (max_q_per_seq > total_q) return BI_ERR_INVALID_SHAPE;
@@ -555,7 +555,7 @@ int bi_attn_prefill_i16(const bi_attn_shape* s, const void* q, const void* k_new
   }
 }
 
-int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
+bi_status bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new, const void* v_new,
                        const int32_t* kv_len, const int32_t* block_table, void* k_cache,
                        void* v_cache, float* k_scale, float* v_scale, void* out, float* lse,
                        int32_t max_kv_len, void* workspace, size_t workspace_bytes,
@@ -564,7 +564,7 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
     const int c = check_decode(s, q, k_new, v_new, kv_len, block_table, k_cache, v_cache, out, lse,
                                max_kv_len, workspace);
     if (c < 0) return BI_OK;
-    if (c != BI_OK) return c;
+    if (c != BI_OK) return (bi_status)c;
     if (!k_scale || !v_scale) return BI_ERR_NULL_POINTER;
     if (!aligned16(k_scale) || !aligned16(v_scale)) return BI_ERR_INVALID_SHAPE;
     const int ns = (max_kv_len + bi::kSplit - 1) / bi::kSplit;
@@ -586,7 +586,7 @@ int bi_attn_decode_i16(const bi_attn_shape* s, const void* q, const void* k_new,
 
 // ---- error-compensated matmul ------------------------------------------------
 
-int bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream) {
+bi_status bi_matmul_ec_pack_w(const float* w, void* w3, int64_t k, int64_t n, void* stream) {
   try {
     if (k < 0 || n < 0) return BI_ERR_INVALID_SHAPE;
     if (k == 0 || n == 0) return BI_OK;
@@ -603,7 +603,7 @@ size_t bi_matmul_ec_workspace_bytes(int64_t m, int64_t k) {
   return (size_t)m * (size_t)(3 * k) * 2;
 }
 
-int bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtype, int64_t m,
+bi_status bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtype, int64_t m,
                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
   try {
     if (m < 0 || n < 0 || k < 0) return BI_ERR_INVALID_SHAPE;
@@ -615,7 +615,7 @@ int bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtyp
     const int64_t kk = (a_dtype == BI_DTYPE_F32 ? 3 : 2) * k;
     const int st = check_matmul(workspace, w3, c, c_dtype, m, n, kk);
     if (st < 0) return BI_OK;
-    if (st != BI_OK) return st;
+    if (st != BI_OK) return (bi_status)st;
     if (k > 0 && a == nullptr) return BI_ERR_NULL_POINTER;
     if (!aligned16(a)) return BI_ERR_INVALID_SHAPE;
     if (workspace_bytes < (size_t)m * (size_t)kk * 2) return BI_ERR_WORKSPACE_TOO_SMALL;
@@ -633,7 +633,7 @@ int bi_matmul_ec(const void* a, int a_dtype, const void* w3, void* c, int c_dtyp
   }
 }
 
-int bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream) {
+bi_status bi_argmax(const float* x, int32_t* out, int64_t rows, int64_t n, void* stream) {
   try {
     if (rows < 0 || n < 0) return BI_ERR_INVALID_SHAPE;
     if (rows == 0) return BI_OK;
