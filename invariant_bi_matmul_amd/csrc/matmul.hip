@@ -63,13 +63,17 @@ namespace bi {
 namespace {
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int BK_ = kMatmulBK,
-          int PP_ = 0>
+          int PP_ = 0, bool ROWSKIP_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_,
                        STAGES = STAGES_;
   // PP: the two halves of the workgroup take turns (1; 2 also raises the
   // issuing priority of the half in its MFMA phase)
   static constexpr int PP = PP_;
+  // ROWSKIP (one 32-row block per wave): a single row-tile launch issues only
+  // the A loads that fill rows below M, skips the MFMAs of waves with no such
+  // row, and keeps the ring depth
+  static constexpr bool ROWSKIP = ROWSKIP_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 32, NI = WN / 32;
   static constexpr int KS = BK / 16;                  // MFMA k-steps per k-tile
@@ -80,8 +84,11 @@ struct TileCfg {
   static constexpr int A_ROW = BK * 2, W_ROW = BN * 2;
   static constexpr int A_CPR = BK / 8, W_CPR = BN / 8;  // 16-byte chunks per row
   static constexpr int GROUP_M = 4;                   // row-tiles per raster group
-  static_assert(BK == 64 || BK == 32, "A swizzles exist for 128- and 64-byte rows");
-  static_assert(kMatmulBK % BK == 0, "k-tiles divide the k granularity of the interface");
+  static_assert(BK == 128 || BK == 64 || BK == 32,
+                "A swizzles exist for 256-, 128- and 64-byte rows");
+  static_assert(kMatmulBK % BK == 0 || BK == 2 * kMatmulBK,
+                "k-tiles divide the k granularity of the interface (or take two of it: such a "
+                "tile runs only where k is a multiple of its k-tile)");
   static_assert(BN == 256 || BN == 128 || BN == 64 || BN == 32,
                 "W swizzles exist for 32, 16, 8 and 4 chunks per k row");
   static_assert(A_LOADS * NT * 16 == A_BYTES && W_LOADS * NT * 16 == W_BYTES, "tile/threads");
@@ -93,25 +100,34 @@ struct TileCfg {
   // the same LDS holds: 6 stages for NA = 1, 4 for NA = 2, 3 for NA = 4.
   static constexpr int a_bytes(int na) { return na * NT * 16; }
   static constexpr int stage_bytes(int na) { return a_bytes(na) + W_BYTES; }
-  static constexpr int ring(int na) { return STAGES * STAGE / stage_bytes(na); }
+  static constexpr int ring(int na) { return ROWSKIP ? STAGES : STAGES * STAGE / stage_bytes(na); }
+  // rows of A one load (one per thread) fills
+  static constexpr int A_ROWS_PER_LOAD = NT * 16 / A_ROW;
   // the single-row-tile variants (live row blocks, fewer A loads) need two
   // 32-row blocks per wave and A load i filling rows 64i .. 64i+63
   static constexpr bool LIVE_VARIANTS = MI == 2 && A_LOADS == 4 && BM / A_LOADS == 64;
   static_assert(PP == 0 || (!LIVE_VARIANTS && WAVES_M == 2 && WAVES_N == 4 && STAGES >= 3),
                 "the alternating halves are the two wave rows");
+  static_assert(!ROWSKIP || (MI == 1 && !LIVE_VARIANTS && PP == 0), "row skipping");
 };
 // The main tile, a larger one for launches with at least a round of them,
 // and four smaller ones for launches whose main-tile grid would leave CUs
 // idle: 256 x 256 (eight 128 x 64 waves; 32-wide k-tiles, so that four stages
 // fit; its wave rows alternate MFMA and memory phases), 128 x 128 (four 64 x 64 waves, one per SIMD), 128 x 64 (four 64 x 32
 // waves), 64 x 64 (four 32 x 32 waves) and 64 x 32 (two 32 x 32 waves, twice
-// the workgroups on W of a small-M launch).
+// the workgroups on W of a small-M launch).  Where k is a multiple of 128 the
+// 64 x 32 tile takes 128-wide k-tiles (half the barriers and waits per byte)
+// and, in a single row-tile launch, issues only the A loads of rows below M
+// (rows 0..7, 0..15, 0..31 or all 64) and skips the MFMAs of a wave with no
+// such row; a k-tile only groups the same ascending 16-wide MFMA steps.
 using Tile = TileCfg<256, 128, 4, 2, 3>;
 using TileL = TileCfg<256, 256, 2, 4, 4, 32, 2>;
 using TileM = TileCfg<128, 128, 2, 2, 3>;
 using TileN = TileCfg<128, 64, 2, 2, 4>;
 using TileS = TileCfg<64, 64, 2, 2, 4>;
 using TileT = TileCfg<64, 32, 2, 1, 6>;
+// 64 x 32 with 128-wide k-tiles and row skipping, for k a multiple of 128
+using TileTW = TileCfg<64, 32, 2, 1, 6, 128, 0, true>;
 
 // A in LDS: [BM rows][CPR chunks of 16 B]; chunk c of row r sits at
 // c ^ swz_a(r).  An MFMA operand read takes one chunk position from each of
@@ -119,10 +135,12 @@ using TileT = TileCfg<64, 32, 2, 1, 6>;
 // then fall on 16 different 16-byte bank groups: for 128-byte rows row pairs
 // already differ by 128 bytes and the XOR spreads the 8 rows of each parity,
 // for 64-byte rows row quads differ by 64 bytes and the XOR spreads the 4
-// rows of each residue mod 4.
+// rows of each residue mod 4, and 256-byte rows, which all start on the same
+// bank, are spread by the XOR with r mod 16.
 template <int CPR>
 __device__ __forceinline__ int swz_a(int r) {
-  if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
+  if constexpr (CPR == 16) return r & 15;
+  else if constexpr (CPR == 8) return (r ^ (r >> 3)) & 7;
   else return (r >> 2) & 3;
 }
 // W in LDS: [BK k rows][CPR chunks of 16 B]; chunk c of k row k sits at
@@ -407,6 +425,14 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
   // issued either: NA = 1 (M <= 64), 2 (M <= 128) or all 4 A loads per k-tile.
   // Every row an MFMA of a live block reads lies below 64 * ceil(M / 64).
   int live = MI, na = T::A_LOADS;
+  if (T::ROWSKIP && tiles_m == 1) {
+    // one 32-row block per wave: live if it holds a row below M; the A loads
+    // cover the first ceil(M / rows per load) row groups, rounded up to 1, 2,
+    // 4 or all of them
+    live = __builtin_amdgcn_readfirstlane(M > wave_m * T::WM ? 1 : 0);
+    const int need = (M + T::A_ROWS_PER_LOAD - 1) / T::A_ROWS_PER_LOAD;
+    na = need <= 1 ? 1 : (need <= 2 ? 2 : (need <= 4 ? 4 : T::A_LOADS));
+  }
   if (T::LIVE_VARIANTS && tiles_m == 1) {
     const int rows = M - wave_m * T::WM;
     live = __builtin_amdgcn_readfirstlane(rows <= 0 ? 0 : (rows >= MI * 32 ? MI : (rows + 31) / 32));
@@ -498,9 +524,9 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
   };
   // one variant for the whole launch: (live blocks of this wave, A loads)
   auto run_live = [&](auto nc) __attribute__((always_inline)) {
-    if (!T::LIVE_VARIANTS || live == MI)
+    if (!(T::LIVE_VARIANTS || T::ROWSKIP) || live == MI)
       run(std::integral_constant<int, MI>{}, nc);
-    else if constexpr (T::LIVE_VARIANTS) {
+    else if constexpr (T::LIVE_VARIANTS || T::ROWSKIP) {
       if (live == 1)
         run(std::integral_constant<int, 1>{}, nc);
       else
@@ -579,6 +605,16 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
   };
   if constexpr (T::PP != 0 && !SPLIT) {
     run_pp();
+  } else if constexpr (T::ROWSKIP && !SPLIT) {
+    constexpr int NA4 = T::A_LOADS > 4 ? 4 : T::A_LOADS;
+    if (na == 1)
+      run_live(std::integral_constant<int, 1>{});
+    else if (na == 2)
+      run_live(std::integral_constant<int, 2>{});
+    else if (na == 4)
+      run_live(std::integral_constant<int, NA4>{});
+    else
+      run_live(std::integral_constant<int, T::A_LOADS>{});
   } else if constexpr (SPLIT || !T::LIVE_VARIANTS) {  // the comparator keeps the one full ring
     run_live(std::integral_constant<int, T::A_LOADS>{});
   } else {
@@ -680,7 +716,9 @@ hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int6
   int bm, bn;
   int64_t grid;
   matmul_tile(m, n, &bm, &bn, &grid);
-  if (bm == TileT::BM && bn == TileT::BN)
+  if (bm == TileT::BM && bn == TileT::BN && k % TileTW::BK == 0)
+    launch_tile<TileTW>(a, w, c, c_f32, m, n, k, grid, st);
+  else if (bm == TileT::BM && bn == TileT::BN)
     launch_tile<TileT>(a, w, c, c_f32, m, n, k, grid, st);
   else if (bm == TileS::BM)
     launch_tile<TileS>(a, w, c, c_f32, m, n, k, grid, st);

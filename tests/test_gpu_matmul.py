@@ -49,12 +49,13 @@ def test_row_invariance_across_m(n):
     wd = to_dev(w)
     full = _mm(a, None, w_dev=wd)
     # the workload's M, M on both sides of the single-row-tile variants (A
-    # loads for rows 0..63, 0..127, all 256), and M that select each tile
-    # (N = 4096: 64 x 32 up to 128, 64 x 64 to 256, 128 x 64 to 512, 128 x 128
-    # to 1024, then the main tile; N = 14336: 64 x 64 to 64, 128 x 128 to 256,
-    # the main tile to 1536, then 256 x 256)
-    for m in list(M_SET[:-1]) + [33, 65, 100, 128, 129, 200, 255, 257, 513, 768, 1024, 1025,
-                                 1536, 1537]:
+    # loads for rows 0..63, 0..127, all 256; for the 64 x 32 tile's 128-wide
+    # k-tiles rows 0..7, 0..15, 0..31, all 64, and its second wave idle up to
+    # 32), and M that select each tile (N = 4096: 64 x 32 up to 128, 64 x 64 to
+    # 256, 128 x 64 to 512, 128 x 128 to 1024, then the main tile; N = 14336:
+    # 64 x 64 to 64, 128 x 128 to 256, the main tile to 1536, then 256 x 256)
+    for m in list(M_SET[:-1]) + [8, 9, 17, 32, 33, 65, 100, 128, 129, 200, 255, 257, 513, 768,
+                                 1024, 1025, 1536, 1537]:
         c = _mm(a[:m], None, w_dev=wd)
         assert np.array_equal(c, full[:m]), m
     # a row at many different positions inside tiles and batches
@@ -101,7 +102,11 @@ def test_one_hot_rows_select_w():
                                    (500, 2056, 192), (1000, 2056, 128), (1100, 4104, 128),
                                    (2100, 4104, 128),
                                    # fewer k-tiles than the 256 x 256 tile's ring holds
-                                   (2100, 4104, 64)])
+                                   (2100, 4104, 64),
+                                   # the 64 x 32 tile with 128-wide k-tiles (k % 128 == 0:
+                                   # one k-tile; fewer than its ring; A rows 0..31 only)
+                                   # and with 64-wide ones (k % 128 == 64)
+                                   (2, 4104, 128), (17, 4104, 384), (9, 4104, 320)])
 def test_ragged_shapes(orc, m, n, k):
     import invariant_bi_matmul_amd as bi
     tile = {(500, 2056): (128, 64), (1000, 2056): (128, 128), (1100, 4104): (256, 128),
