@@ -236,8 +236,10 @@ def comparators(wl):
     warm, timed in turns (best of two).  Matmul: the decoder stack's projection shapes at M = 1, 16, 64 (the
     decode batches) and the step's 2048 x 4096 x 14336, each beside split-K
     (bi_matmul's tile with k split to fill idle CUs) and the vendor GEMM
-    (torch.matmul, not batch-invariant); `stack_token_ms` adds up one decode
-    token's projections (32 layers + lm_head) for each kernel."""
+    (torch.matmul, not batch-invariant), and both invariant and split-K again
+    with the weight in the strip layout (bi_matmul_pack_w, as the stack holds
+    it); `stack_token_ms` adds up one decode token's projections (32 layers +
+    lm_head) for each kernel."""
     import torch
     bi, synth, dev = wl.bi, wl.synth, wl.dev
     out = {}
@@ -250,7 +252,8 @@ def comparators(wl):
     most = max(lib.bix_matmul_workspace_bytes(m, n, k, 0) for _, m, k, n in shapes)
     ws = torch.empty(most // 4 + 16, dtype=torch.float32, device=dev)
     ws_cache = {}
-    per_token = {m: {"invariant": 0.0, "splitk": 0.0, "vendor": 0.0} for m in (1, 16, 64)}
+    per_token = {m: {"invariant": 0.0, "splitk": 0.0, "vendor": 0.0, "invariant_packed": 0.0,
+                     "splitk_packed": 0.0} for m in (1, 16, 64)}
     for label, m, k, n in shapes:
         if (k, n) not in ws_cache:
             ws_cache[(k, n)] = (wl.w if (k, n) == (K, N) else
@@ -260,26 +263,35 @@ def comparators(wl):
         a = a_big[:m, :k].contiguous()
         c = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
         need = lib.bix_matmul_workspace_bytes(m, n, k, 0)
-        ti, tc, tv = time_alternating([
+        wp = bi.matmul_pack_w(w)  # the strip layout, as the stack holds its weights
+        ti, tc, tv, tip, tcp = time_alternating([
             lambda: bi.matmul(a, w, out=c),
             lambda: bi.bix_matmul_splitk(a, w, out=c, workspace=ws[:need // 4 + 4]),
-            lambda: torch.matmul(a, w, out=c)])
+            lambda: torch.matmul(a, w, out=c),
+            lambda: bi.matmul_packed(a, wp, out=c),
+            lambda: bi.bix_matmul_splitk(a, wp, out=c, workspace=ws[:need // 4 + 4])])
+        del wp
         splits = max(1, need // (4 * m * n))
         if splits == 1:
             # no CU left idle: the comparator launches the invariant kernel itself,
             # and the two timings differ only by noise (clock, order)
             ti = tc = min(ti, tc)
+            tip = tcp = min(tip, tcp)
         out["matmul_" + label] = {"invariant_ms": ti, "splitk_ms": tc, "vendor_ms": tv,
+                                  "invariant_packed_ms": tip, "splitk_packed_ms": tcp,
                                   "splitk_slices": splits,
                                   "invariant_over_splitk": ti / tc,
-                                  "invariant_over_vendor": ti / tv}
+                                  "invariant_over_vendor": ti / tv,
+                                  "invariant_over_splitk_packed": tip / tcp}
         if label != shapes[0][0]:
             reps = 1 if label.startswith("lm_head") else 32
-            for kind, t in (("invariant", ti), ("splitk", tc), ("vendor", tv)):
+            for kind, t in (("invariant", ti), ("splitk", tc), ("vendor", tv),
+                            ("invariant_packed", tip), ("splitk_packed", tcp)):
                 per_token[m][kind] += reps * t
     for m, r in per_token.items():
         r["invariant_over_splitk"] = r["invariant"] / r["splitk"]
         r["invariant_over_vendor"] = r["invariant"] / r["vendor"]
+        r["invariant_over_splitk_packed"] = r["invariant_packed"] / r["splitk_packed"]
     out["stack_token_ms"] = per_token
     del ws, a_big, ws_cache
     for r in (1, 16, 2048):
@@ -522,7 +534,8 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
     matmul: M in {1,2,7,16,64,256,512,2048}, N in {4096, 14336}, K=4096:
     TFLOP/s, fraction of the bf16 peak, of the roofline min(peak, AI x 8 TB/s)
     and the grid-fill ceiling of the tile bi_matmul picks; beside it the vendor
-    GEMM (torch.matmul, not batch-invariant) on the same buffers.  RMSNorm: R in
+    GEMM (torch.matmul, not batch-invariant) on the same buffers and
+    bi_matmul_packed on the same weights in the strip layout (packed_ms).  RMSNorm: R in
     {1..16384 powers of two, 3, 7, 1000, 16383}, H in {4096, 8192}.  Decode:
     L in {512, 4096, 32768} x B in {1..64}, lengths ragged U{L/2..L} with one
     probe at L, shuffled 16-token pages.  Prefill: one sequence of L tokens,
@@ -540,6 +553,7 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
         sets = max(1, -(-ROTATE_BYTES // wbytes))
         ws = [synth.device_normal_bf16((K, n), 0.0, 0.125, 0, "sweep.w%d.%d" % (n, i), dev)
               for i in range(sets)]
+        wps = [bi.matmul_pack_w(w) for w in ws]  # the same weights in the strip layout
         for m in (1, 2, 7, 16, 64, 256, 512, 2048):
             a = a_full[:m].contiguous()
             cs = [torch.empty(m, n, dtype=torch.bfloat16, device=dev) for _ in range(sets)]
@@ -548,6 +562,8 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
             gms = time_graph(fns, max(40, 2 * sets))
             vfns = [(lambda w=w, c=c: torch.matmul(a, w, out=c)) for w, c in zip(ws, cs)]
             vms = time_rotating(vfns, max(40, 2 * sets))
+            pfns = [(lambda w=w, c=c: bi.matmul_packed(a, w, out=c)) for w, c in zip(wps, cs)]
+            pms = time_rotating(pfns, max(40, 2 * sets))
             flops = 2.0 * m * n * K
             by = 2.0 * (m * K + K * n + m * n)
             tf = flops / ms / 1e9
@@ -559,9 +575,10 @@ def sweeps(wl, parts=("matmul", "rmsnorm", "decode", "prefill")):
                 "roofline_TFLOP/s": roof, "roofline_frac": tf / roof,
                 "GB/s": by / ms / 1e6, "tile": "%dx%d" % (tm, tn), "tiles": tiles,
                 "workgroups": wgs, "grid_fill_ceiling": _grid_fill(tiles),
-                "vendor_ms": vms, "invariant_over_vendor": ms / vms, "graph_ms": gms}
+                "vendor_ms": vms, "invariant_over_vendor": ms / vms, "graph_ms": gms,
+                "packed_ms": pms, "packed_roofline_frac": flops / pms / 1e9 / roof}
             del cs
-        del ws
+        del ws, wps
     for h in (4096, 8192) if "rmsnorm" in parts else ():
         log("sweep: rmsnorm H=%d" % h)
         rows_big = ROTATE_BYTES // (2 * h)

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define BI_ABI_VERSION 4
+#define BI_ABI_VERSION 5
 
 typedef enum {
   BI_OK = 0,
@@ -119,6 +119,22 @@ bi_status bi_rmsnorm(const void* x, const void* gamma, void* y, float* rstd, int
  */
 bi_status bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n, int64_t k,
               void* stream);
+
+/* The same product with W in the strip layout written by bi_matmul_pack_w:
+ * wp = bf16 [n/32][k][32], strip j holding columns 32j .. 32j+31 of w, each
+ * strip contiguous along k.  A launch whose workgroups each stream one or two
+ * strips (small m) then reads whole bursts of HBM rather than 64-byte pieces
+ * of w's rows.  c is bitwise what bi_matmul(a, w, ...) gives: the same tiles,
+ * MFMA and k order, only the global addresses of w differ.  Requires
+ * n % 32 == 0 as well as bi_matmul's conditions (else BI_ERR_UNSUPPORTED).
+ * A layout choice of the approach table's MatMul row, not a new reduction. */
+bi_status bi_matmul_packed(const void* a, const void* wp, void* c, int c_dtype, int64_t m,
+                           int64_t n, int64_t k, void* stream);
+
+/* wp[j][r][i] = w[r][32j + i]: w bf16 [k, n] row-major into the strip layout
+ * (k * n bf16 values, caller-owned, no overlap with w).  n % 32 == 0,
+ * k <= 2^22, n <= 2^24 (else BI_ERR_UNSUPPORTED); k or n = 0 is a no-op. */
+bi_status bi_matmul_pack_w(const void* w, void* wp, int64_t k, int64_t n, void* stream);
 
 /* The output tile bi_matmul uses for an m x n product on the current device
  * (tile_m x tile_n) and the workgroups it launches.  Host-only; any pointer
@@ -245,6 +261,10 @@ size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split
 bi_status bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
                       int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                       void* stream);
+/* The same comparator with W in bi_matmul_pack_w's strip layout (n % 32 == 0). */
+bi_status bix_matmul_splitk_packed(const void* a, const void* wp, void* c, int c_dtype,
+                                   int64_t m, int64_t n, int64_t k, int32_t split_k,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* bix_attn_decode_splitkv: decode whose key range is cut into `num_splits`
  * equal parts per sequence (num_splits <= 0: chosen from B and max_kv_len to

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "BIError", "lib_path", "debug_lib_path", "load", "load_library", "abi_version", "rmsnorm",
-    "matmul", "attn_workspace_bytes",
+    "matmul", "matmul_pack_w", "matmul_packed", "attn_workspace_bytes",
     "attn_prefill", "attn_decode", "attn_decode_noalloc", "DECODE_SCRATCH_BYTES", "AttnShape",
     "SPLIT", "PAGE",
     "bix_rmsnorm_splitrow", "matmul_tile", "bix_matmul_splitk",
@@ -90,6 +90,10 @@ def load_library(path: str):
         "bi_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "bi_rmsnorm": (ctypes.c_int, [P, P, P, P, i64, i64, f32, P]),
         "bi_matmul": (ctypes.c_int, [P, P, P, ctypes.c_int, i64, i64, i64, P]),
+        "bi_matmul_packed": (ctypes.c_int, [P, P, P, ctypes.c_int, i64, i64, i64, P]),
+        "bi_matmul_pack_w": (ctypes.c_int, [P, P, i64, i64, P]),
+        "bix_matmul_splitk_packed": (ctypes.c_int, [P, P, P, ctypes.c_int, i64, i64, i64,
+                                                    ctypes.c_int32, P, ctypes.c_size_t, P]),
         "bi_attn_workspace_bytes": (sz, [SP, i64, i32]),
         "bi_attn_prefill": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, i64, i32, P]),
         "bi_attn_decode": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, i32, P, sz, P]),
@@ -223,6 +227,40 @@ def matmul(a: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None,
     return c
 
 
+def matmul_pack_w(w: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """w bf16 [k, n] -> the strip layout bf16 [n/32, k, 32] (bi_matmul_pack_w)."""
+    _dev(w, "w", torch.bfloat16)
+    if w.dim() != 2:
+        raise ValueError("need w [k, n]")
+    k, n = w.shape
+    if n % 32 != 0:
+        raise ValueError("n must be a multiple of 32")
+    wp = torch.empty(n // 32, k, 32, dtype=torch.bfloat16, device=w.device) if out is None else \
+        _dev(out, "out", torch.bfloat16, (n // 32, k, 32))
+    _check("bi_matmul_pack_w", load().bi_matmul_pack_w(_ptr(w), _ptr(wp), k, n, _stream()))
+    return wp
+
+
+def matmul_packed(a: torch.Tensor, wp: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  out_dtype: torch.dtype = torch.bfloat16):
+    """C = A @ W with W given as matmul_pack_w(W) ([n/32, k, 32]); bitwise
+    equal to matmul(a, W)."""
+    _dev(a, "a", torch.bfloat16)
+    _dev(wp, "wp", torch.bfloat16)
+    if a.dim() != 2 or wp.dim() != 3 or wp.shape[2] != 32 or a.shape[1] != wp.shape[1]:
+        raise ValueError("need a [m, k] and wp [n/32, k, 32]")
+    m, k = a.shape
+    n = wp.shape[0] * 32
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    c = torch.empty(m, n, dtype=out_dtype, device=a.device) if out is None else \
+        _dev(out, "out", out_dtype, (m, n))
+    code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
+    _check("bi_matmul_packed", load().bi_matmul_packed(_ptr(a), _ptr(wp), _ptr(c), code, m, n, k,
+                                                       _stream()))
+    return c
+
+
 def matmul_tile(m: int, n: int):
     """(tile_m, tile_n, workgroups) of bi_matmul for an m x n product on the
     current device (bix_matmul_tile; host-only, launches nothing)."""
@@ -235,11 +273,13 @@ def matmul_tile(m: int, n: int):
 def bix_matmul_splitk(a, w, split_k: int = 0, out=None, out_dtype=torch.bfloat16,
                       workspace=None):
     """Non-invariant comparator: split-K with ``split_k`` slices (0 = chosen
-    from the grid size)."""
+    from the grid size).  A 3-D ``w`` is taken as matmul_pack_w's strip layout
+    [n/32, k, 32] (bix_matmul_splitk_packed)."""
     _dev(a, "a", torch.bfloat16)
     _dev(w, "w", torch.bfloat16)
     m, k = a.shape
-    n = w.shape[1]
+    packed = w.dim() == 3
+    n = w.shape[0] * 32 if packed else w.shape[1]
     c = torch.empty(m, n, dtype=out_dtype, device=a.device) if out is None else \
         _dev(out, "out", out_dtype, (m, n))
     lib = load()
@@ -247,7 +287,8 @@ def bix_matmul_splitk(a, w, split_k: int = 0, out=None, out_dtype=torch.bfloat16
     if workspace is None:
         workspace = torch.empty(max(need, 16) // 4 + 4, dtype=torch.float32, device=a.device)
     code = DTYPE_F32 if out_dtype == torch.float32 else DTYPE_BF16
-    _check("bix_matmul_splitk", lib.bix_matmul_splitk(
+    fn = lib.bix_matmul_splitk_packed if packed else lib.bix_matmul_splitk
+    _check("bix_matmul_splitk", fn(
         _ptr(a), _ptr(w), _ptr(c), code, m, n, k, int(split_k), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream()))
     return c

@@ -188,6 +188,33 @@ bi_status bi_matmul(const void* a, const void* w, void* c, int c_dtype, int64_t 
   }
 }
 
+bi_status bi_matmul_pack_w(const void* w, void* wp, int64_t k, int64_t n, void* stream) {
+  try {
+    if (k < 0 || n < 0) return BI_ERR_INVALID_SHAPE;
+    if (n % 32 != 0 || k > (int64_t)1 << 22 || n > (int64_t)1 << 24) return BI_ERR_UNSUPPORTED;
+    if (k == 0 || n == 0) return BI_OK;
+    if (w == nullptr || wp == nullptr) return BI_ERR_NULL_POINTER;
+    if (!aligned16(w) || !aligned16(wp)) return BI_ERR_INVALID_SHAPE;
+    return hip_status(bi::launch_matmul_pack_w(w, wp, k, n, (hipStream_t)stream));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
+bi_status bi_matmul_packed(const void* a, const void* wp, void* c, int c_dtype, int64_t m,
+                           int64_t n, int64_t k, void* stream) {
+  try {
+    const int s = check_matmul(a, wp, c, c_dtype, m, n, k);
+    if (s < 0) return BI_OK;
+    if (s != BI_OK) return (bi_status)s;
+    if (n % 32 != 0) return BI_ERR_UNSUPPORTED;
+    return hip_status(bi::launch_matmul(a, wp, c, c_dtype == BI_DTYPE_F32, m, n, k,
+                                        (hipStream_t)stream, true));
+  } catch (...) {
+    return BI_ERR_INTERNAL;
+  }
+}
+
 bi_status bix_matmul_tile(int64_t m, int64_t n, int32_t* tile_m, int32_t* tile_n, int64_t* workgroups) {
   if (m < 1 || n < 1) return BI_ERR_INVALID_SHAPE;
   int bm, bn;
@@ -206,13 +233,14 @@ size_t bix_matmul_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t split
   return (size_t)split_k * (size_t)m * (size_t)n * sizeof(float);
 }
 
-bi_status bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m, int64_t n,
-                      int64_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+static bi_status matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m,
+                               int64_t n, int64_t k, int32_t split_k, void* workspace,
+                               size_t workspace_bytes, void* stream, bool packed) {
   try {
     const int s = check_matmul(a, w, c, c_dtype, m, n, k);
     if (s < 0) return BI_OK;
     if (s != BI_OK) return (bi_status)s;
+    if (packed && n % 32 != 0) return BI_ERR_UNSUPPORTED;
     if (k == 0) return BI_ERR_UNSUPPORTED;
     if (split_k <= 0) split_k = bi::matmul_splitk_auto(m, n, k);
     if (split_k > k / bi::kMatmulBK || split_k > 65535) return BI_ERR_UNSUPPORTED;
@@ -221,10 +249,24 @@ bi_status bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, 
     if (workspace_bytes < (size_t)split_k * (size_t)m * (size_t)n * sizeof(float))
       return BI_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(bi::launch_matmul_splitk(a, w, c, c_dtype == BI_DTYPE_F32, m, n, k, split_k,
-                                               (float*)workspace, (hipStream_t)stream));
+                                               (float*)workspace, (hipStream_t)stream, packed));
   } catch (...) {
     return BI_ERR_INTERNAL;
   }
+}
+
+bi_status bix_matmul_splitk(const void* a, const void* w, void* c, int c_dtype, int64_t m,
+                            int64_t n, int64_t k, int32_t split_k, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return matmul_splitk(a, w, c, c_dtype, m, n, k, split_k, workspace, workspace_bytes, stream,
+                       false);
+}
+
+bi_status bix_matmul_splitk_packed(const void* a, const void* wp, void* c, int c_dtype, int64_t m,
+                                   int64_t n, int64_t k, int32_t split_k, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return matmul_splitk(a, wp, c, c_dtype, m, n, k, split_k, workspace, workspace_bytes, stream,
+                       true);
 }
 
 // ---------------------------------------------------------------------------

@@ -23,8 +23,11 @@ int device_cus();
 constexpr int kMatmulBK = 64;
 // The tile launch_matmul uses for an m x n product (bm x bn) and its grid.
 void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid);
+// packed: w is in the strip layout of launch_matmul_pack_w
 hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
-                         int64_t k, hipStream_t st);
+                         int64_t k, hipStream_t st, bool packed = false);
+// W [k, n] row-major -> [n/32][k][32] (n % 32 == 0)
+hipError_t launch_matmul_pack_w(const void* w, void* wp, int64_t k, int64_t n, hipStream_t st);
 int matmul_splitk_auto(int64_t m, int64_t n, int64_t k);
 hipError_t launch_mfma_loop(int64_t iters, int workgroups, bool varied, float* sink,
                             hipStream_t st);
@@ -37,7 +40,8 @@ hipError_t launch_check_attn_tables(const int32_t* kv_len, const int32_t* cu_q, 
 hipError_t launch_read_stream(const void* p, int64_t bytes, int workgroups, uint32_t* sink,
                               hipStream_t st);
 hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,
-                                int64_t n, int64_t k, int split_k, float* ws, hipStream_t st);
+                                int64_t n, int64_t k, int split_k, float* ws, hipStream_t st,
+                                bool packed = false);
 
 // ---- attention -------------------------------------------------------------
 constexpr int kSplit = 256;   // fixed key split

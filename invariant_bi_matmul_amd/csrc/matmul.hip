@@ -178,7 +178,12 @@ __device__ __forceinline__ void raster_tile(uint32_t id, int tiles_m, int tiles_
 // tiles back to back through one continuous stream of k-tiles: the ring
 // loads the next tile's first k-tiles while the current tile finishes.  The
 // split-K comparator launches one workgroup per (tile, slice) instead.
-template <class T, bool SPLIT>
+// PW: W comes in the strip layout of bi_matmul_pack_w, [n/32][k][32]: each
+// 32-column strip is contiguous along k, so a small-M launch, whose workgroups
+// each stream one or two strips, reads whole bursts instead of 64-byte pieces
+// of 8 KiB rows.  Only the global addresses differ; what reaches LDS, and so
+// every MFMA operand, is the same as with the row-major W.
+template <class T, bool SPLIT, bool PW = false>
 __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ W,
                                                              void* __restrict__ C, int M, int N,
@@ -313,10 +318,14 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
     for (int i = 0; i < T::W_LOADS; ++i) {
       const int q = i * NT + wave * 64 + lane;
       const int k = q / T::W_CPR, c = (q % T::W_CPR) ^ swz_w<T::W_CPR>(q / T::W_CPR);
-      w_off[i] = (uint32_t)(((int64_t)k * N + min(n0 + c * 8, N - 8) - n0) * 2);
+      const int n = min(n0 + c * 8, N - 8);  // the chunk's first column
+      if constexpr (PW)  // strip n/32, row k, column n mod 32 (n0 starts a strip)
+        w_off[i] = (uint32_t)((((int64_t)(n / 32 - n0 / 32) * K + k) * 32 + n % 32) * 2);
+      else
+        w_off[i] = (uint32_t)(((int64_t)k * N + n - n0) * 2);
     }
     a_base = (const uint8_t*)(A + (int64_t)m0 * K);
-    w_base = (const uint8_t*)(W + n0);
+    w_base = (const uint8_t*)(PW ? W + (int64_t)(n0 / 32) * K * 32 : W + n0);
   };
   const int64_t total = (int64_t)count * nk;  // stream length
   int64_t ipos = 0;                            // stream position of the next load
@@ -342,7 +351,8 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
     constexpr int NA = decltype(nc)::value;
     const int kt = kt0 + ikt;
     const uint8_t* ab = a_base + (int64_t)kt * (BK * 2);
-    const uint8_t* wb = w_base + (int64_t)kt * BK * N * 2;
+    // elements from one k row of W to the next: 32 in a strip, else N
+    const uint8_t* wb = w_base + (int64_t)kt * BK * (PW ? 32 : N) * 2;
     const uint32_t sb = lds0 + stage * T::stage_bytes(NA) + wave * 1024;
 #pragma unroll
     for (int i = 0; i < NA; ++i)
@@ -628,6 +638,19 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
   wait_vmcnt_le<0>();  // no LDS write may outlive the workgroup
 }
 
+// W [k, n] row-major -> the strip layout [n/32][k][32]; one 16-byte chunk
+// (8 columns) per thread, read along W's rows.
+__global__ __launch_bounds__(256) void bi_matmul_pack_w_kernel(const uint16_t* __restrict__ w,
+                                                                uint16_t* __restrict__ wp,
+                                                                int64_t k, int64_t n) {
+  const int64_t chunks = k * (n / 8);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= chunks) return;
+  const int64_t row = i / (n / 8), c8 = i % (n / 8);
+  const u32x4 v = *(const u32x4*)(w + row * n + c8 * 8);
+  *(u32x4*)(wp + ((c8 / 4) * k + row) * 32 + (c8 % 4) * 8) = v;
+}
+
 // Sum split-K partials in slice order, then round.
 __global__ __launch_bounds__(256) void bix_matmul_reduce_kernel(const float* __restrict__ ws,
                                                                  void* __restrict__ C,
@@ -680,10 +703,15 @@ static int64_t tile_count(int64_t m, int64_t n) {
 // ascending 16-wide steps), so the choice changes no bits.
 template <class T>
 static void launch_tile(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
-                        int64_t k, int64_t grid, hipStream_t st) {
-  hipLaunchKernelGGL((bi_matmul_kernel<T, false>), dim3((unsigned)grid), dim3(T::NT), 0, st,
-                     (const uint16_t*)a, (const uint16_t*)w, c, (int)m, (int)n, (int)k,
-                     c_f32 ? 1 : 0, 0);
+                        int64_t k, int64_t grid, bool packed, hipStream_t st) {
+  if (packed)
+    hipLaunchKernelGGL((bi_matmul_kernel<T, false, true>), dim3((unsigned)grid), dim3(T::NT), 0,
+                       st, (const uint16_t*)a, (const uint16_t*)w, c, (int)m, (int)n, (int)k,
+                       c_f32 ? 1 : 0, 0);
+  else
+    hipLaunchKernelGGL((bi_matmul_kernel<T, false>), dim3((unsigned)grid), dim3(T::NT), 0, st,
+                       (const uint16_t*)a, (const uint16_t*)w, c, (int)m, (int)n, (int)k,
+                       c_f32 ? 1 : 0, 0);
 }
 
 void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid) {
@@ -712,24 +740,32 @@ void matmul_tile(int64_t m, int64_t n, int* bm, int* bn, int64_t* grid) {
 }
 
 hipError_t launch_matmul(const void* a, const void* w, void* c, bool c_f32, int64_t m, int64_t n,
-                         int64_t k, hipStream_t st) {
+                         int64_t k, hipStream_t st, bool packed) {
   int bm, bn;
   int64_t grid;
   matmul_tile(m, n, &bm, &bn, &grid);
   if (bm == TileT::BM && bn == TileT::BN && k % TileTW::BK == 0)
-    launch_tile<TileTW>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<TileTW>(a, w, c, c_f32, m, n, k, grid, packed, st);
   else if (bm == TileT::BM && bn == TileT::BN)
-    launch_tile<TileT>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<TileT>(a, w, c, c_f32, m, n, k, grid, packed, st);
   else if (bm == TileS::BM)
-    launch_tile<TileS>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<TileS>(a, w, c, c_f32, m, n, k, grid, packed, st);
   else if (bm == TileN::BM && bn == TileN::BN)
-    launch_tile<TileN>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<TileN>(a, w, c, c_f32, m, n, k, grid, packed, st);
   else if (bm == TileM::BM)
-    launch_tile<TileM>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<TileM>(a, w, c, c_f32, m, n, k, grid, packed, st);
   else if (bn == TileL::BN)
-    launch_tile<TileL>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<TileL>(a, w, c, c_f32, m, n, k, grid, packed, st);
   else
-    launch_tile<Tile>(a, w, c, c_f32, m, n, k, grid, st);
+    launch_tile<Tile>(a, w, c, c_f32, m, n, k, grid, packed, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_matmul_pack_w(const void* w, void* wp, int64_t k, int64_t n, hipStream_t st) {
+  const int64_t chunks = k * (n / 8);
+  if (chunks > 0)
+    hipLaunchKernelGGL(bi_matmul_pack_w_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256),
+                       0, st, (const uint16_t*)w, (uint16_t*)wp, k, n);
   return hipGetLastError();
 }
 
@@ -754,34 +790,40 @@ int matmul_splitk_auto(int64_t m, int64_t n, int64_t k) {
 // slices that own at least one k-tile (at most split_k).
 template <class T>
 static int launch_split(const void* a, const void* w, float* ws, int64_t m, int64_t n,
-                        int split_k, int64_t k, hipStream_t st) {
+                        int split_k, int64_t k, bool packed, hipStream_t st) {
   const int kt = (int)(k / T::BK);
   const int per = (kt + split_k - 1) / split_k;
   const int used = (kt + per - 1) / per;
   const int64_t tiles = tile_count<T>(m, n);
-  hipLaunchKernelGGL((bi_matmul_kernel<T, true>), dim3((unsigned)tiles, 1, (unsigned)used),
-                     dim3(T::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
-                     (int)m, (int)n, (int)k, 1, per);
+  if (packed)
+    hipLaunchKernelGGL((bi_matmul_kernel<T, true, true>), dim3((unsigned)tiles, 1, (unsigned)used),
+                       dim3(T::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
+                       (int)m, (int)n, (int)k, 1, per);
+  else
+    hipLaunchKernelGGL((bi_matmul_kernel<T, true>), dim3((unsigned)tiles, 1, (unsigned)used),
+                       dim3(T::NT), 0, st, (const uint16_t*)a, (const uint16_t*)w, (void*)ws,
+                       (int)m, (int)n, (int)k, 1, per);
   return used;
 }
 
 hipError_t launch_matmul_splitk(const void* a, const void* w, void* c, bool c_f32, int64_t m,
-                                int64_t n, int64_t k, int split_k, float* ws, hipStream_t st) {
-  if (split_k <= 1) return launch_matmul(a, w, c, c_f32, m, n, k, st);
+                                int64_t n, int64_t k, int split_k, float* ws, hipStream_t st,
+                                bool packed) {
+  if (split_k <= 1) return launch_matmul(a, w, c, c_f32, m, n, k, st, packed);
   int bm, bn;
   int64_t grid;
   matmul_tile(m, n, &bm, &bn, &grid);
   int used;
   if (bm == TileT::BM && bn == TileT::BN)
-    used = launch_split<TileT>(a, w, ws, m, n, split_k, k, st);
+    used = launch_split<TileT>(a, w, ws, m, n, split_k, k, packed, st);
   else if (bm == TileS::BM)
-    used = launch_split<TileS>(a, w, ws, m, n, split_k, k, st);
+    used = launch_split<TileS>(a, w, ws, m, n, split_k, k, packed, st);
   else if (bm == TileN::BM && bn == TileN::BN)
-    used = launch_split<TileN>(a, w, ws, m, n, split_k, k, st);
+    used = launch_split<TileN>(a, w, ws, m, n, split_k, k, packed, st);
   else if (bm == TileM::BM)
-    used = launch_split<TileM>(a, w, ws, m, n, split_k, k, st);
+    used = launch_split<TileM>(a, w, ws, m, n, split_k, k, packed, st);
   else  // 256 x 256 (whose one-slice launch has no registers to spare) or the main tile
-    used = launch_split<Tile>(a, w, ws, m, n, split_k, k, st);
+    used = launch_split<Tile>(a, w, ws, m, n, split_k, k, packed, st);
   const int64_t count = m * n;
   hipLaunchKernelGGL(bix_matmul_reduce_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
                      st, (const float*)ws, c, count, used, c_f32 ? 1 : 0);

@@ -2,8 +2,10 @@
 
 Every arithmetic step is a libbi call:
 - token embedding and row gathers: ``bi_embed``;
-- ``bi_rmsnorm``, then ``bi_matmul`` for the q/k/v, output, gate/up/down and
-  lm_head projections (q|k|v and gate|up as one matmul each by default);
+- ``bi_rmsnorm``, then ``bi_matmul_packed`` (weights in the strip layout of
+  ``bi_matmul_pack_w``; bitwise ``bi_matmul``) for the q/k/v, output,
+  gate/up/down and lm_head projections (q|k|v and gate|up as one matmul each
+  by default);
 - ``bi_qkv_rope`` (split of the fused q|k|v output plus rotary embedding), or
   ``bi_rope``;
 - ``bi_attn_prefill`` / ``bi_attn_decode`` over a paged KV cache (16-token
@@ -36,6 +38,7 @@ import torch
 from . import (PAGE, add, argmax, attn_decode, attn_decode_i16, attn_prefill, attn_prefill_i16,
                attn_workspace_bytes, bix_attn_decode_splitkv, bix_matmul_splitk,
                bix_rmsnorm_splitrow, embed, make_shape, matmul, matmul_ec, matmul_ec_pack_w,
+               matmul_pack_w, matmul_packed,
                qkv_rope, rmsnorm, rope, swiglu, swiglu_pair)
 
 __all__ = ["LlamaConfig", "LAYER_WEIGHTS", "weight_shapes", "Decoder", "DecodeGraph"]
@@ -134,7 +137,14 @@ class Decoder:
         # the tensors each projection multiplies by: the bf16 weight, or the
         # packed [hi; lo; hi] of the fp32 one; q|k|v and gate|up concatenated
         # once when fused
-        prep = matmul_ec_pack_w if mm == "ec" else (lambda t: t)
+        # bf16: each weight whose width is a multiple of 32 goes into the strip
+        # layout (matmul_pack_w), which a small-batch step streams in whole
+        # bursts; the products are bitwise those of the row-major weight
+        if mm == "ec":
+            prep = matmul_ec_pack_w
+        else:
+            def prep(t):
+                return matmul_pack_w(t) if t.shape[1] % 32 == 0 else t
         self.proj = []
         for lw in weights["layers"]:
             pw = {"wo": prep(lw["wo"]), "w_down": prep(lw["w_down"])}
@@ -162,14 +172,15 @@ class Decoder:
         self.comparator = comparator
         if comparator:
             self._norm = lambda x, g: bix_rmsnorm_splitrow(x, g, cfg.eps)
-            self._mm = lambda a, w, **kw: bix_matmul_splitk(a, w, **kw)
+            self._mm = lambda a, w, **kw: bix_matmul_splitk(a, w, **kw)  # either layout
         elif mm == "ec":
             self._norm = lambda x, g: rmsnorm(x, g, cfg.eps)
             self._mm = lambda a, w3, out_dtype=torch.bfloat16: matmul_ec(a, w3,
                                                                          out_dtype=out_dtype)
         else:
             self._norm = lambda x, g: rmsnorm(x, g, cfg.eps)
-            self._mm = matmul
+            self._mm = lambda a, w, **kw: (matmul_packed(a, w, **kw) if w.dim() == 3
+                                           else matmul(a, w, **kw))
 
     # ---- KV page bookkeeping ---------------------------------------------------
     def add_sequence(self, sid: int):

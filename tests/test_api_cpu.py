@@ -43,11 +43,11 @@ def test_debug_build_exports_the_same_functions():
     dbg = ctypes.CDLL(_build.DEBUG_LIB)
     for n in declared_functions():
         assert hasattr(dbg, n), n
-    assert dbg.bi_abi_version() == 4
+    assert dbg.bi_abi_version() == 5
 
 
 def test_version_and_status_strings(lib):
-    assert lib.bi_abi_version() == 4
+    assert lib.bi_abi_version() == 5
     for s in range(7):
         assert lib.bi_status_string(s)
     assert lib.bi_status_string(99) == b"unknown status"
@@ -80,6 +80,21 @@ def test_matmul_validation(lib):
     assert f(None, None, None, 0, 0, 4096, 4096, None) == OK
     assert lib.bix_matmul_workspace_bytes(8, 4096, 4096, 4) == 4 * 8 * 4096 * 4
     assert lib.bix_matmul_splitk(_p(), _p(), _p(), 0, 8, 4096, 4096, 4, _p(), 1024, None) == WS
+
+
+def test_matmul_packed_validation(lib):
+    f = lib.bi_matmul_packed
+    assert f(_p(), _p(), _p(), 0, 4, 4104, 4096, None) == UNSUP     # n % 32
+    assert f(_p(), _p(), _p(), 0, 4, 4096, 100, None) == UNSUP      # k % 64
+    assert f(_p(), _p(), _p(), 0, -4, 4096, 4096, None) == SHAPE
+    assert f(_p(), None, _p(), 0, 4, 4096, 4096, None) == NULLP
+    assert f(None, None, None, 0, 0, 4096, 4096, None) == OK
+    g = lib.bi_matmul_pack_w
+    assert g(_p(), _p(), 4096, 4104, None) == UNSUP                  # n % 32
+    assert g(_p(), _p(), -1, 4096, None) == SHAPE
+    assert g(None, _p(), 4096, 4096, None) == NULLP
+    assert g(_p(0x1008), _p(), 4096, 4096, None) == SHAPE            # alignment
+    assert g(None, None, 0, 4096, None) == OK                         # empty: no-op
 
 
 def test_matmul_tile_choice(lib):

@@ -136,3 +136,42 @@ def test_repeat_bitwise():
     c0 = _mm(a, None, w_dev=wd)
     for _ in range(20):
         assert np.array_equal(_mm(a, None, w_dev=wd), c0)
+
+
+def test_pack_w_layout():
+    import invariant_bi_matmul_amd as bi
+    _, w = synth.matmul_inputs(1, 4128, 320, seed=7)
+    wp = bi.matmul_pack_w(to_dev(w))
+    expect = w.reshape(320, 4128 // 32, 32).transpose(1, 0, 2)
+    assert np.array_equal(bits_of(wp), expect)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    # every tile: 64 x 32 (128- and 64-wide k-tiles, row skipping), 64 x 64, 128 x 64,
+    # 128 x 128, 256 x 128, 256 x 256, with N past the last full tile where n % 32 == 0
+    (1, 4096, 4096), (9, 4096, 14336), (33, 4128, 320), (100, 4096, 256), (200, 4096, 192),
+    (300, 4096, 128), (600, 4096, 128), (1100, 4096, 128), (2100, 4128, 128),
+    (2048, 14336, 4096), (257, 2080, 128)])
+def test_packed_equals_row_major(m, n, k):
+    import invariant_bi_matmul_amd as bi
+    a, w = synth.matmul_inputs(m, n, k, seed=8)
+    wd = to_dev(w)
+    ad = to_dev(a)
+    wp = bi.matmul_pack_w(wd)
+    for dt in (torch.bfloat16, torch.float32):
+        ref = bi.matmul(ad, wd, out_dtype=dt)
+        c = poison_like(torch.empty(m, n, dtype=dt, device=ad.device))
+        bi.matmul_packed(ad, wp, out=c, out_dtype=dt)
+        assert torch.equal(c.view(torch.int32 if dt == torch.float32 else torch.int16),
+                           ref.view(torch.int32 if dt == torch.float32 else torch.int16)), (m, n, k, dt)
+
+
+def test_packed_splitk_comparator_equals_row_major():
+    import invariant_bi_matmul_amd as bi
+    a, w = synth.matmul_inputs(16, 4096, 4096, seed=9)
+    ad, wd = to_dev(a), to_dev(w)
+    wp = bi.matmul_pack_w(wd)
+    for s in (1, 4, 16):
+        r = bi.bix_matmul_splitk(ad, wd, split_k=s)
+        p = bi.bix_matmul_splitk(ad, wp, split_k=s)
+        assert torch.equal(r.view(torch.int16), p.view(torch.int16)), s
