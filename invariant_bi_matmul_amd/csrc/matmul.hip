@@ -71,8 +71,9 @@ struct TileCfg {
   // issuing priority of the half in its MFMA phase)
   static constexpr int PP = PP_;
   // ROWSKIP (one 32-row block per wave): a single row-tile launch issues only
-  // the A loads that fill rows below M, skips the MFMAs of waves with no such
-  // row, and keeps the ring depth
+  // the A loads that fill rows below M and keeps the ring depth; every wave
+  // still runs its MFMAs (a wave whose rows are all past M computes rows that
+  // are never stored), so both waves run one instruction stream
   static constexpr bool ROWSKIP = ROWSKIP_;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, MI = WM / 32, NI = WN / 32;
@@ -118,8 +119,8 @@ struct TileCfg {
 // the workgroups on W of a small-M launch).  Where k is a multiple of 128 the
 // 64 x 32 tile takes 128-wide k-tiles (half the barriers and waits per byte)
 // and, in a single row-tile launch, issues only the A loads of rows below M
-// (rows 0..7, 0..15, 0..31 or all 64) and skips the MFMAs of a wave with no
-// such row; a k-tile only groups the same ascending 16-wide MFMA steps.
+// (rows 0..7, 0..15, 0..31 or all 64); a k-tile only groups the same
+// ascending 16-wide MFMA steps.
 using Tile = TileCfg<256, 128, 4, 2, 3>;
 using TileL = TileCfg<256, 256, 2, 4, 4, 32, 2>;
 using TileM = TileCfg<128, 128, 2, 2, 3>;
@@ -436,10 +437,8 @@ __global__ __launch_bounds__(T::NT) void bi_matmul_kernel(const uint16_t* __rest
   // Every row an MFMA of a live block reads lies below 64 * ceil(M / 64).
   int live = MI, na = T::A_LOADS;
   if (T::ROWSKIP && tiles_m == 1) {
-    // one 32-row block per wave: live if it holds a row below M; the A loads
-    // cover the first ceil(M / rows per load) row groups, rounded up to 1, 2,
-    // 4 or all of them
-    live = __builtin_amdgcn_readfirstlane(M > wave_m * T::WM ? 1 : 0);
+    // the A loads cover the first ceil(M / rows per load) row groups, rounded
+    // up to 1, 2, 4 or all of them
     const int need = (M + T::A_ROWS_PER_LOAD - 1) / T::A_ROWS_PER_LOAD;
     na = need <= 1 ? 1 : (need <= 2 ? 2 : (need <= 4 ? 4 : T::A_LOADS));
   }
