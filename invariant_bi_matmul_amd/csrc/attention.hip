@@ -1080,8 +1080,8 @@ void bi_attn_decode_partial_kernel(
 // sequential is the fma chain of l and of each output dim (thread d owns dim
 // d), over the same values in the same order as the fold step by step, so the
 // bits are those of fold_coef / fold_apply applied in turn.  A chunk (CH <= D
-// splits: 32 when every sequence fits in 33 splits, else D) has all its
-// records requested before its chain starts.
+// splits: 16 when every sequence fits in 17 splits, 32 when in 33, else D) has
+// all its records requested before its chain starts.
 template <int D, int CH>
 __global__ __launch_bounds__(D) void bi_attn_combine_kernel(const float* __restrict__ ws,
                                                             const int32_t* __restrict__ kv_len,
@@ -1614,7 +1614,10 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const void* k_ne
       BI_DECODE(128, true);
     else
       BI_DECODE(128, false);
-    if (max_splits <= 33)
+    if (max_splits <= 17)
+      hipLaunchKernelGGL((bi_attn_combine_kernel<128, 16>), grid2, dim3(128), 0, st,
+                         (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
+    else if (max_splits <= 33)
       hipLaunchKernelGGL((bi_attn_combine_kernel<128, 32>), grid2, dim3(128), 0, st,
                          (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
     else
@@ -1625,7 +1628,10 @@ hipError_t launch_attn_decode(const AttnDims& s, const void* q, const void* k_ne
       BI_DECODE(64, true);
     else
       BI_DECODE(64, false);
-    if (max_splits <= 33)
+    if (max_splits <= 17)
+      hipLaunchKernelGGL((bi_attn_combine_kernel<64, 16>), grid2, dim3(64), 0, st,
+                         (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
+    else if (max_splits <= 33)
       hipLaunchKernelGGL((bi_attn_combine_kernel<64, 32>), grid2, dim3(64), 0, st,
                          (const float*)ws, kv_len, (uint16_t*)out, lse, s.nq, max_splits, kSplit);
     else
